@@ -1,0 +1,422 @@
+#!/usr/bin/env python3
+"""Benchmark: quantized decoder projections on one MI355X.
+
+Headline (`value`): W8A8 decode at one token -- the Llama-3.1-8B projection set
+(per layer q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 14336x4096,
+down 4096x14336), 32 layers with distinct weights (6.98 GB of int8, far above
+the 256 MB Infinity Cache).  One step = one decoded token through all 32
+layers: 4 per-token int8 activation quantizations and 7 one-row products per
+layer (352 kernels), replayed as one HIP graph.  value = algorithmic bytes of
+the step / step time, in GB/s.
+
+Also reported (`secondary`): M=512 (and 1024) prefill TOPS for W8A8 int8, FP8
+per-channel (Llama shapes) and FP8 block (Qwen3-8B shapes); per-shape GEMV
+bandwidth; small-M (4..32) fused-projection bandwidth.
+
+`roofline` is for the dominant kernel, the int8 one-row product: achieved =
+algorithmic bytes per launch / average launch duration measured with HIP events
+around a graph of the 224 products.  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same decode workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_INT8_PEAK_TOPS = 5000.0   # dense int8, POP/s -> TOPS
+MFMA_FP8_PEAK_TOPS = 5000.0    # dense fp8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--quick", action="store_true", help="headline only (no secondary sweeps, no CPU baseline)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU-oracle sample")
+    return ap.parse_args()
+
+
+class Launcher:
+    """Pre-marshalled C-ABI calls (raw pointers), so a step is a list of calls."""
+
+    def __init__(self, Q, torch):
+        self.L = Q.lib()
+        self.torch = torch
+        self.calls = []
+
+    def stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def quant_int8(self, x, q, s):
+        M, K = x.shape
+        self.calls.append((self.L.qlin_quant_act_int8, (x.data_ptr(), M, K, q.data_ptr(), s.data_ptr())))
+
+    def quant_fp8(self, x, q, s, group):
+        M, K = x.shape
+        self.calls.append((self.L.qlin_quant_act_fp8, (x.data_ptr(), M, K, group, q.data_ptr(), s.data_ptr())))
+
+    def gemm(self, fn, qx, sx, qw, sw, y, M, N, K, out=0, path=0):
+        f = getattr(self.L, fn + "_ex")
+        self.calls.append((f, (qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
+                               M, N, K, out, path)))
+
+    def run(self, calls=None):
+        st = self.stream()
+        for f, a in (self.calls if calls is None else calls):
+            r = f(*a, st)
+            if r != 0:
+                raise RuntimeError(f"{f.__name__} failed with status {r}")
+
+
+def capture(torch, fn, use_graph=True):
+    """Return a callable replaying fn (a HIP graph when use_graph)."""
+    if not use_graph:
+        return fn
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g.replay
+
+
+def time_events(torch, fn, reps):
+    """Milliseconds per call of fn, from HIP events on the current stream."""
+    st = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(st)
+    for _ in range(reps):
+        fn()
+    b.record(st)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+def decode_bytes(N, K):
+    """Algorithmic bytes of one one-row product: weights once, row scales,
+    the quantized activation row and its scale, the bf16 output."""
+    return N * K + 2 * N + K + 4 + 2 * N
+
+
+def quant_bytes(M, K):
+    return 2 * M * K + M * K + 4 * M
+
+
+def build_decode(torch, Q, W, layers, dev):
+    """32 layers of int8 projections with distinct weights + per-layer inputs."""
+    L = Launcher(Q, torch)
+    G = Launcher(Q, torch)          # products only (for the roofline)
+    gen = torch.Generator(device=dev)
+    shapes = dict((n, (N, K)) for n, N, K in W.LLAMA_8B)
+    bufs = []
+    step_bytes = 0
+    gemv_bytes = 0
+    per_shape = {}
+    for layer in range(layers):
+        gen.manual_seed(100 + layer)
+        lw = {}
+        for name, N, K in W.LLAMA_8B:
+            qw = W.torch_w_int8(torch, gen, N, K, dev)
+            sw = W.torch_scale_bf16(torch, gen, (N,), dev)
+            y = torch.empty((1, N), dtype=torch.int16, device=dev)
+            lw[name] = (qw, sw, y)
+        for group in W.INPUT_GROUPS:
+            K = shapes[group[0]][1]
+            x = W.torch_x_bf16(torch, gen, 1, K, dev)
+            q = torch.empty((1, K), dtype=torch.int8, device=dev)
+            s = torch.empty((1,), dtype=torch.float32, device=dev)
+            L.quant_int8(x, q, s)
+            step_bytes += quant_bytes(1, K)
+            lw["in_" + group[0]] = (x, q, s)
+            for name in group:
+                qw, sw, y = lw[name]
+                N, K2 = shapes[name]
+                L.gemm("qlin_gemm_w8a8", q, s, qw, sw, y, 1, N, K2)
+                G.gemm("qlin_gemm_w8a8", q, s, qw, sw, y, 1, N, K2)
+                b = decode_bytes(N, K2)
+                step_bytes += b
+                gemv_bytes += b
+                per_shape.setdefault(name, []).append((q, s, qw, sw, y, N, K2))
+        bufs.append(lw)
+    return L, G, bufs, step_bytes, gemv_bytes, per_shape
+
+
+def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
+    """Projection sweeps at M tokens: a launcher with quant + product per input
+    group and one with products only.  variant: int8 | fp8_row | fp8_block."""
+    shapes = W.LLAMA_8B if variant != "fp8_block" else W.QWEN3_8B
+    shp = dict((n, (N, K)) for n, N, K in shapes)
+    full = Launcher(Q, torch)
+    prod = Launcher(Q, torch)
+    gen = torch.Generator(device=dev)
+    ops = 0
+    keep = []
+    fn = {"int8": "qlin_gemm_w8a8", "fp8_row": "qlin_gemm_fp8_rowwise", "fp8_block": "qlin_gemm_fp8_block"}[variant]
+    for layer in range(layers):
+        gen.manual_seed(seed0 + layer)
+        for group in W.INPUT_GROUPS:
+            K = shp[group[0]][1]
+            x = W.torch_x_bf16(torch, gen, M, K, dev)
+            if variant == "int8":
+                q = torch.empty((M, K), dtype=torch.int8, device=dev)
+                s = torch.empty((M,), dtype=torch.float32, device=dev)
+                full.quant_int8(x, q, s)
+            else:
+                q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                g = 128 if variant == "fp8_block" else 0
+                s = torch.empty((M, K // 128) if g else (M,), dtype=torch.float32, device=dev)
+                full.quant_fp8(x, q, s, g)
+            keep += [x, q, s]
+            for name in group:
+                N, _ = shp[name]
+                if variant == "int8":
+                    qw = W.torch_w_int8(torch, gen, N, K, dev)
+                else:
+                    qw = W.torch_w_e4m3(torch, gen, N, K, dev)
+                sws = (N // 128, K // 128) if variant == "fp8_block" else (N,)
+                sw = W.torch_scale_bf16(torch, gen, sws, dev)
+                y = torch.empty((M, N), dtype=torch.int16, device=dev)
+                keep += [qw, sw, y]
+                full.gemm(fn, q, s, qw, sw, y, M, N, K)
+                prod.gemm(fn, q, s, qw, sw, y, M, N, K)
+                ops += 2 * M * N * K
+    return full, prod, ops, keep
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle leg
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(torch, W, bufs, budget_s):
+    """Time the CPU oracle (as it stands) on a bounded sample of the decode
+    workload: whole layers in order, until the time budget is spent.  Also
+    returns the largest error of the GPU outputs against the oracle."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    shapes = dict((n, (N, K)) for n, N, K in W.LLAMA_8B)
+    t_total = 0.0
+    nbytes = 0
+    nproj = 0
+    max_rel = 0.0
+    exact_order = True
+    layers_done = 0
+    for lw in bufs:
+        for group in W.INPUT_GROUPS:
+            x = lw["in_" + group[0]][0].cpu().numpy().view(np.uint16)
+            for name in group:
+                qw_t, sw_t, y_t = lw[name]
+                qw = qw_t.cpu().numpy()
+                sw = sw_t.cpu().numpy().view(np.uint16)
+                N, K = shapes[name]
+                t0 = time.perf_counter()
+                yb, y_exact, qx, sx, acc = O.linear_w8a8(x, qw, sw)
+                t_total += time.perf_counter() - t0
+                nbytes += decode_bytes(N, K)
+                nproj += 1
+                yg = y_t.cpu().numpy().view(np.uint16)
+                yf = (yg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                max_rel = max(max_rel, float(np.max(np.abs(yf - y_exact)) / np.max(np.abs(y_exact))))
+                exact_order &= bool(np.array_equal(yg, O.epilogue_f32_order(acc, sx, sw)))
+        layers_done += 1
+        if t_total >= budget_s:
+            break
+    return {
+        "value": nbytes / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{layers_done} of 32 decode layers ({nproj} projections with their int8 activation "
+                  f"quantization), oracle wall time {t_total:.2f} s",
+    }, max_rel, exact_order
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_linear_layers_token_amd as Q
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    use_graph = not args.no_graph
+
+    # ---- headline: decode, M = 1, 32 distinct layers -------------------------
+    log("building decode workload (32 layers, int8)")
+    L, G, bufs, step_bytes, gemv_bytes, per_shape = build_decode(torch, Q, W, W.LLAMA_8B_LAYERS, dev)
+    torch.cuda.synchronize()
+    step = capture(torch, L.run, use_graph)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} decode steps")
+    t0 = time.perf_counter()
+    ms = time_events(torch, step, args.steps)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = step_bytes / (ms * 1e-3) / 1e9
+    log(f"decode step {ms:.4f} ms (wall {wall_ms:.4f} ms)  {value:.1f} GB/s")
+
+    # ---- roofline of the dominant kernel: the int8 one-row product ----------
+    gemv_only = capture(torch, G.run, use_graph)
+    for _ in range(2):
+        gemv_only()
+    n_launch = len(G.calls)
+    ms_gemv = time_events(torch, gemv_only, max(3, args.steps // 2))
+    avg_launch_us = ms_gemv * 1e3 / n_launch
+    bytes_per_launch = gemv_bytes / n_launch
+    achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemv_kernel<VAR_INT8,...> (qlin_gemm_w8a8 at M=1)",
+                "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 3),
+                "launches": n_launch}
+    log(f"gemv-only: {n_launch} launches, avg {avg_launch_us:.3f} us, {achieved:.1f} GB/s")
+
+    secondary = {}
+    if not args.quick:
+        # per-shape one-row bandwidth (all 32 layers of one projection back to back)
+        shape_gbs = {}
+        for name, items in per_shape.items():
+            P = Launcher(Q, torch)
+            for q, s, qw, sw, y, N, K in items:
+                P.gemm("qlin_gemm_w8a8", q, s, qw, sw, y, 1, N, K)
+            fn = capture(torch, P.run, use_graph)
+            fn()
+            t = time_events(torch, fn, 5)
+            shape_gbs[name] = round(len(items) * decode_bytes(N, K) / (t * 1e-3) / 1e9, 1)
+        secondary["decode_gemv_gbs_per_shape"] = shape_gbs
+        log(f"per-shape GB/s {shape_gbs}")
+
+        # small batch (M = 4..32) on the fused projections, int8
+        small = {}
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(200)
+        fused = [(n, N, K) for n, N, K in W.LLAMA_8B_FUSED]
+        wts = {n: (W.torch_w_int8(torch, gen, N, K, dev), W.torch_scale_bf16(torch, gen, (N,), dev))
+               for n, N, K in fused}
+        for M in (4, 8, 16, 32):
+            P = Launcher(Q, torch)
+            nb = 0
+            ops = 0
+            keep = []
+            for n, N, K in fused:
+                x = W.torch_x_bf16(torch, gen, M, K, dev)
+                q = torch.empty((M, K), dtype=torch.int8, device=dev)
+                s = torch.empty((M,), dtype=torch.float32, device=dev)
+                y = torch.empty((M, N), dtype=torch.int16, device=dev)
+                keep += [x, q, s, y]
+                Q.qlin_quant_act_int8(x, q, s)
+                P.gemm("qlin_gemm_w8a8", q, s, wts[n][0], wts[n][1], y, M, N, K)
+                nb += N * K + 2 * N + M * K + 4 * M + 2 * M * N
+                ops += 2 * M * N * K
+            fn = capture(torch, P.run, use_graph)
+            fn()
+            t = time_events(torch, fn, 10)
+            small[str(M)] = {"gbs": round(nb / (t * 1e-3) / 1e9, 1), "tops": round(ops / (t * 1e-3) / 1e12, 2),
+                             "us_per_layer": round(t * 1e3, 2)}
+            del keep
+        secondary["small_m_fused_int8"] = small
+        log(f"small-M fused {small}")
+        del wts
+
+        # prefill TOPS
+        for variant, peak in (("int8", MFMA_INT8_PEAK_TOPS), ("fp8_row", MFMA_FP8_PEAK_TOPS),
+                              ("fp8_block", MFMA_FP8_PEAK_TOPS)):
+            for M in (512, 1024):
+                full, prod, ops, keep = prefill_layer_set(torch, Q, W, variant, M, 4, dev,
+                                                          {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
+                f_full = capture(torch, full.run, use_graph)
+                f_prod = capture(torch, prod.run, use_graph)
+                f_full()
+                f_prod()
+                t_full = time_events(torch, f_full, 5)
+                t_prod = time_events(torch, f_prod, 5)
+                key = f"prefill_{variant}_M{M}"
+                secondary[key] = {
+                    "tops_gemm": round(ops / (t_prod * 1e-3) / 1e12, 1),
+                    "frac_gemm": round(ops / (t_prod * 1e-3) / 1e12 / peak, 4),
+                    "tops_with_quant": round(ops / (t_full * 1e-3) / 1e12, 1),
+                    "ms_per_layer_gemm": round(t_prod / 4, 4),
+                    "shapes": "qwen3-8b" if variant == "fp8_block" else "llama-3.1-8b",
+                }
+                log(f"{key}: {secondary[key]}")
+                del keep, full, prod, f_full, f_prod
+                torch.cuda.synchronize()
+
+    cpu = None
+    if not args.quick:
+        log("CPU oracle sample")
+        cpu, max_rel, exact = cpu_baseline(torch, W, bufs, args.cpu_seconds)
+        secondary["max_rel_err_vs_oracle"] = max_rel
+        secondary["bf16_bitexact_vs_oracle_f32_order"] = exact
+        log(f"cpu baseline {cpu}; max rel err {max_rel:.3g}; bitexact {exact}")
+
+    out = {
+        "metric": "W8A8 M=1 GEMV HBM GB/s + M=512 int8/fp8 TOPS, Llama-8B projection set",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3.1-8B W8A8 decode, M=1, 32 layers with distinct int8 weights; per token 128 "
+                        "per-token int8 activation quantizations + 224 one-row products (q, k, v, o, gate, up, "
+                        "down), " + ("replayed as one HIP graph" if use_graph else "launched eagerly"),
+            "bytes_per_step": step_bytes,
+            "hip_graph": use_graph,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

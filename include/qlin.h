@@ -1,0 +1,185 @@
+/*
+ * qlin -- quantized decoder projections for AMD Instinct MI355X (gfx950).
+ *
+ * One operation in three schemes:
+ *
+ *     y[m, n] = (s_x[m] * s_w[n]) * sum_k q_x[m, k] * q_w[n, k]
+ *
+ *   W8A8 int8   -- "Llama 3.1 8B Instruct W8A8" model card, intro and section
+ *                  "Loading": int8 weights with one bf16 scale per output row,
+ *                  inputs rounded to int8 one token at a time, int8 products
+ *                  summed in int32.
+ *   FP8 rowwise -- "Llama 3.1 8B Instruct FP8" page intro and the
+ *                  "Meta-Llama-3.1-8B-Instruct-FP8-dynamic" README ("Model
+ *                  Optimizations", "Creation"): E4M3 weights with one scale
+ *                  per output channel, per-token dynamic E4M3 inputs.
+ *   FP8 block   -- "Qwen3 8B FP8" model card, intro and "Loading": E4M3
+ *                  weights with one bf16 scale per 128x128 block (a
+ *                  multiplier), inputs rounded to E4M3 128 at a time; widths
+ *                  are multiples of 128.  Per K block kb:
+ *                  y[m, n] = sum_kb s_x[m, kb] * s_w[n/128, kb] * P_kb[m, n].
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are caller-owned DEVICE memory.  The library never allocates,
+ *    frees or synchronizes; work is enqueued on `stream` (0 = the null
+ *    stream) and the call returns at once.  Outputs must not overlap inputs.
+ *  - Matrices are contiguous and row-major with K fastest: x / q_x are
+ *    [M, K], q_w is [N, K] (one row per output channel), y is [M, N].
+ *  - Matrix pointers (x, q, q_x, q_w, y) must be 16-byte aligned; f32 scale
+ *    pointers 4-byte aligned; bf16 scale pointers 2-byte aligned.
+ *  - K must be a positive multiple of 16 and at most QLIN_MAX_K; M and N are
+ *    >= 0 and at most QLIN_MAX_MN.  M == 0 or N == 0 is a no-op returning
+ *    QLIN_OK.
+ *  - bf16 values are passed as their uint16 bit patterns; E4M3 values as
+ *    uint8 codes (OCP E4M3: bias 7, max 448, 0x7F/0xFF NaN, no infinities).
+ *  - Errors are returned, never thrown.  Arguments are validated before any
+ *    work is enqueued: on an error return nothing was launched and no output
+ *    was touched.  QLIN_ERR_HIP means the launch itself failed; the HIP error
+ *    code is then available from qlin_last_hip_error() on the calling thread.
+ *  - Calls are thread-safe; calls on different streams may run concurrently.
+ */
+#ifndef QLIN_H_
+#define QLIN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's own hipStream_t. */
+typedef struct ihipStream_t* hipStream_t;
+
+#define QLIN_ABI_VERSION 1
+#define QLIN_MAX_K  131072          /* 127 * 128 * K stays below 2^31 */
+#define QLIN_MAX_MN (1 << 24)
+
+typedef enum qlin_status {
+    QLIN_OK = 0,
+    QLIN_ERR_NULL = 1,         /* a required pointer is null */
+    QLIN_ERR_SHAPE = 2,        /* bad size: K <= 0, K % 16, > max, block sizes not multiples of 128, bad group */
+    QLIN_ERR_ALIGN = 3,        /* a pointer misses its required alignment */
+    QLIN_ERR_UNSUPPORTED = 4,  /* output mode or forced path not available for this call */
+    QLIN_ERR_HIP = 5,          /* the HIP runtime rejected the launch */
+    QLIN_ERR_ALIAS = 6         /* an output range overlaps an input range */
+} qlin_status;
+
+/* Output element type written to y. */
+typedef enum qlin_out {
+    QLIN_OUT_BF16 = 0,  /* bf16, round to nearest even of the f32 result */
+    QLIN_OUT_I32 = 1,   /* int8 schemes only: the raw int32 accumulator sum_k q_x*q_w */
+    QLIN_OUT_F32 = 2    /* the f32 result before the bf16 rounding */
+} qlin_out;
+
+/* Kernel regime.  AUTO follows the pages' split ("Loading" sections of the
+ * W8A8 and Qwen3 model cards): one row -> a kernel that reads each weight
+ * byte once; up to 32 rows -> matrix cores streaming the weights; longer
+ * inputs -> a tiled matrix-core GEMM.  The other values force one kernel at
+ * any M (for testing each kernel outside its default regime). */
+typedef enum qlin_path {
+    QLIN_PATH_AUTO = 0,
+    QLIN_PATH_GEMV = 1,   /* M must be 1 */
+    QLIN_PATH_SMALL = 2,  /* M must be <= 32 */
+    QLIN_PATH_LARGE = 3   /* any M */
+} qlin_path;
+
+/* ---------------------------------------------------------------------- */
+/* Dynamic activation quantizers                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Per-token int8 quantization (W8A8 model card, intro and "Loading": inputs
+ * rounded to int8 a token at a time).  For each row m of x (bf16 [M, K]):
+ *   a = max_k |x[m,k]|;  s[m] = fl32(a / 127);  inv = fl32(127 / a) (0 if a == 0)
+ *   q[m,k] = clamp(round_half_even(fl32(x[m,k] * inv)), -127, 127)
+ * q: int8 [M, K] (written), s: f32 [M] (written).  Non-finite inputs and rows
+ * whose 127/a overflows f32 are outside the contract (no fault, values
+ * unspecified). */
+qlin_status qlin_quant_act_int8(const uint16_t* x, int64_t M, int64_t K,
+                                int8_t* q, float* s, hipStream_t stream);
+
+/* Dynamic FP8 (OCP E4M3) quantization.
+ *   group == 0:   one scale per token (FP8-dynamic README, "Creation" recipe:
+ *                 per-token, dynamic, symmetric); s is f32 [M].
+ *   group == 128: one scale per 128 consecutive inputs, groups aligned at
+ *                 k = 128 g (Qwen3 8B FP8 model card, "Loading"); K % 128 == 0;
+ *                 s is f32 [M, K/128] row-major.
+ * Per token or group: s = fl32(a / 448), inv = fl32(448 / a) (0 if a == 0),
+ *   q = nearest E4M3 code of clamp(fl32(x * inv), -448, 448), ties to even,
+ *   sign of zero kept. */
+qlin_status qlin_quant_act_fp8(const uint16_t* x, int64_t M, int64_t K, int32_t group,
+                               uint8_t* q, float* s, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Products                                                               */
+/* ---------------------------------------------------------------------- */
+
+/* One-token W8A8 product (M = 1; W8A8 model card, "Loading": one row in a
+ * kernel that reads each byte once).
+ *   q_x int8 [K], s_x f32 [1], q_w int8 [N, K], s_w bf16 [N], y [N].
+ *   acc[n] = sum_k q_x[k] q_w[n,k] (exact int32);
+ *   BF16/F32: y[n] = fl32(acc) * fl32(s_x * s_w[n]), rounded to bf16 for BF16;
+ *   I32: y[n] = acc. */
+qlin_status qlin_gemv_w8a8(const int8_t* q_x, const float* s_x,
+                           const int8_t* q_w, const uint16_t* s_w,
+                           void* y, int64_t N, int64_t K, qlin_out out,
+                           hipStream_t stream);
+
+/* W8A8 product for any M (same formula per row m; s_x f32 [M], y [M, N]).
+ * Dispatch (AUTO): M == 1 -> the one-row kernel; 2..32 -> matrix-core
+ * streaming kernel; larger -> tiled matrix-core GEMM.  A fused projection
+ * (e.g. q/k/v or gate/up) is the same call on row-concatenated q_w / s_w. */
+qlin_status qlin_gemm_w8a8(const int8_t* q_x, const float* s_x,
+                           const int8_t* q_w, const uint16_t* s_w,
+                           void* y, int64_t M, int64_t N, int64_t K, qlin_out out,
+                           hipStream_t stream);
+qlin_status qlin_gemm_w8a8_ex(const int8_t* q_x, const float* s_x,
+                              const int8_t* q_w, const uint16_t* s_w,
+                              void* y, int64_t M, int64_t N, int64_t K, qlin_out out,
+                              qlin_path path, hipStream_t stream);
+
+/* FP8 E4M3 product with per-token activation scales s_x f32 [M] and
+ * per-output-channel weight scales s_w bf16 [N] ("Llama 3.1 8B Instruct FP8"
+ * intro; FP8-dynamic README "Model Optimizations").  q_x uint8 [M, K],
+ * q_w uint8 [N, K].  acc = sum_k e4m3(q_x) e4m3(q_w) in f32 (any order);
+ * y = acc * fl32(s_x[m] * s_w[n]).  Out modes: BF16, F32. */
+qlin_status qlin_gemm_fp8_rowwise(const uint8_t* q_x, const float* s_x,
+                                  const uint8_t* q_w, const uint16_t* s_w,
+                                  void* y, int64_t M, int64_t N, int64_t K, qlin_out out,
+                                  hipStream_t stream);
+qlin_status qlin_gemm_fp8_rowwise_ex(const uint8_t* q_x, const float* s_x,
+                                     const uint8_t* q_w, const uint16_t* s_w,
+                                     void* y, int64_t M, int64_t N, int64_t K, qlin_out out,
+                                     qlin_path path, hipStream_t stream);
+
+/* FP8 E4M3 product with 128x128 weight-block scales and 1x128 activation
+ * group scales (Qwen3 8B FP8 model card, intro and "Loading"; the weight
+ * scale multiplies).  N % 128 == 0 and K % 128 == 0.
+ *   s_x f32 [M, K/128], s_w bf16 [N/128, K/128] (row-major).
+ *   y[m,n] = sum_kb (s_x[m,kb] * s_w[n/128,kb]) * P_kb[m,n], f32 accumulate,
+ *   where P_kb is the E4M3 dot product over k in [128 kb, 128 kb + 128).
+ * Out modes: BF16, F32. */
+qlin_status qlin_gemm_fp8_block(const uint8_t* q_x, const float* s_x,
+                                const uint8_t* q_w, const uint16_t* s_w,
+                                void* y, int64_t M, int64_t N, int64_t K, qlin_out out,
+                                hipStream_t stream);
+qlin_status qlin_gemm_fp8_block_ex(const uint8_t* q_x, const float* s_x,
+                                   const uint8_t* q_w, const uint16_t* s_w,
+                                   void* y, int64_t M, int64_t N, int64_t K, qlin_out out,
+                                   qlin_path path, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Helpers                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Static string naming a status value (never null). */
+const char* qlin_status_string(qlin_status status);
+/* QLIN_ABI_VERSION of the built library. */
+int qlin_abi_version(void);
+/* HIP error code of the last QLIN_ERR_HIP returned on this thread (0 if none). */
+int qlin_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H_ */

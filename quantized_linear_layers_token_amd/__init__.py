@@ -1,0 +1,158 @@
+"""Python binding of libqlin.so (quantized decoder projections on MI355X).
+
+Argument marshalling only: every function below forwards device pointers,
+sizes and the current HIP stream to the C ABI declared in include/qlin.h and
+raises QlinError on a non-OK status.  torch supplies memory and streams; no
+computation happens here.  If the library is not built, importing this package
+fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqlin.so")
+
+QLIN_OK, QLIN_ERR_NULL, QLIN_ERR_SHAPE, QLIN_ERR_ALIGN, QLIN_ERR_UNSUPPORTED, QLIN_ERR_HIP, QLIN_ERR_ALIAS = range(7)
+OUT_BF16, OUT_I32, OUT_F32 = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_LARGE = 0, 1, 2, 3
+ABI_VERSION = 1
+MAX_K = 131072
+
+# Exported symbols and their C signatures (restype, argtypes).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_S = ctypes.c_int
+SIGNATURES = {
+    "qlin_quant_act_int8": (_S, [_P, _I64, _I64, _P, _P, _P]),
+    "qlin_quant_act_fp8": (_S, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "qlin_gemv_w8a8": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _S, _P]),
+    "qlin_gemm_w8a8": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _P]),
+    "qlin_gemm_w8a8_ex": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _S, _P]),
+    "qlin_gemm_fp8_rowwise": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _P]),
+    "qlin_gemm_fp8_rowwise_ex": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _S, _P]),
+    "qlin_gemm_fp8_block": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _P]),
+    "qlin_gemm_fp8_block_ex": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _S, _P]),
+    "qlin_status_string": (ctypes.c_char_p, [_S]),
+    "qlin_abi_version": (_S, []),
+    "qlin_last_hip_error": (_S, []),
+}
+
+
+class QlinError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.qlin_status_string(status).decode() if _lib is not None else str(status)
+        if status == QLIN_ERR_HIP:
+            msg += f" (hip error {_lib.qlin_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def _load():
+    # torch is imported first so that libqlin.so binds (by soname) to the HIP
+    # runtime torch already loaded: one runtime per process, shared streams.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m quantized_linear_layers_token_amd.build` "
+            "(the HIP library is the only implementation; there is no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.qlin_abi_version() != ABI_VERSION:
+        raise ImportError(f"libqlin ABI {lib.qlin_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    """The raw ctypes handle of libqlin.so."""
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != QLIN_OK:
+        raise QlinError(status, where)
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dims2(t, name):
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D tensor")
+    return t.shape[0], t.shape[1]
+
+
+# --------------------------------------------------------------------------
+# Quantizers
+# --------------------------------------------------------------------------
+
+def qlin_quant_act_int8(x, q, s, stream=None):
+    """x: bf16 (or int16 bit patterns) [M, K]; q: int8 [M, K]; s: f32 [M]."""
+    M, K = _dims2(x, "x")
+    _check(_lib.qlin_quant_act_int8(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(stream)), "qlin_quant_act_int8")
+
+
+def qlin_quant_act_fp8(x, q, s, group=0, stream=None):
+    """x: bf16 [M, K]; q: uint8 E4M3 codes [M, K]; s: f32 [M] (group 0) or [M, K/128] (group 128)."""
+    M, K = _dims2(x, "x")
+    _check(_lib.qlin_quant_act_fp8(_ptr(x), M, K, group, _ptr(q), _ptr(s), _stream(stream)), "qlin_quant_act_fp8")
+
+
+# --------------------------------------------------------------------------
+# Products
+# --------------------------------------------------------------------------
+
+def qlin_gemv_w8a8(q_x, s_x, q_w, s_w, y, out=OUT_BF16, stream=None):
+    """q_x int8 [K] or [1, K]; s_x f32 [1]; q_w int8 [N, K]; s_w bf16 [N]; y [N] or [1, N]."""
+    N, K = _dims2(q_w, "q_w")
+    _check(_lib.qlin_gemv_w8a8(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), _ptr(y), N, K, out, _stream(stream)),
+           "qlin_gemv_w8a8")
+
+
+def _mnk(q_x, q_w):
+    M, K = _dims2(q_x, "q_x")
+    N, K2 = _dims2(q_w, "q_w")
+    if K != K2:
+        raise ValueError(f"K mismatch: q_x has {K}, q_w has {K2}")
+    return M, N, K
+
+
+def qlin_gemm_w8a8(q_x, s_x, q_w, s_w, y, out=OUT_BF16, path=PATH_AUTO, stream=None):
+    """q_x int8 [M, K]; s_x f32 [M]; q_w int8 [N, K]; s_w bf16 [N]; y [M, N] (bf16 / i32 / f32)."""
+    M, N, K = _mnk(q_x, q_w)
+    _check(_lib.qlin_gemm_w8a8_ex(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), _ptr(y), M, N, K, out, path,
+                                  _stream(stream)), "qlin_gemm_w8a8")
+
+
+def qlin_gemm_fp8_rowwise(q_x, s_x, q_w, s_w, y, out=OUT_BF16, path=PATH_AUTO, stream=None):
+    """q_x uint8 E4M3 [M, K]; s_x f32 [M]; q_w uint8 E4M3 [N, K]; s_w bf16 [N]; y [M, N]."""
+    M, N, K = _mnk(q_x, q_w)
+    _check(_lib.qlin_gemm_fp8_rowwise_ex(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), _ptr(y), M, N, K, out, path,
+                                         _stream(stream)), "qlin_gemm_fp8_rowwise")
+
+
+def qlin_gemm_fp8_block(q_x, s_x, q_w, s_w, y, out=OUT_BF16, path=PATH_AUTO, stream=None):
+    """q_x uint8 E4M3 [M, K]; s_x f32 [M, K/128]; q_w uint8 E4M3 [N, K]; s_w bf16 [N/128, K/128]; y [M, N]."""
+    M, N, K = _mnk(q_x, q_w)
+    _check(_lib.qlin_gemm_fp8_block_ex(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), _ptr(y), M, N, K, out, path,
+                                       _stream(stream)), "qlin_gemm_fp8_block")
+
+
+def status_string(status: int) -> str:
+    return _lib.qlin_status_string(status).decode()

@@ -1,0 +1,174 @@
+// C ABI: argument validation and regime dispatch.  No allocation, no
+// synchronization; every check runs before the first launch.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/qlin.h"
+#include "qlin_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+Range rng(const void* p, int64_t bytes) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return Range{b, b + (uintptr_t)bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+qlin_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return QLIN_OK;
+    g_last_hip_error = (int)e;
+    return QLIN_ERR_HIP;
+}
+
+bool valid_k(int64_t K) { return K > 0 && (K % 16) == 0 && K <= QLIN_MAX_K; }
+bool valid_mn(int64_t v) { return v >= 0 && v <= QLIN_MAX_MN; }
+
+int out_bytes(qlin_out o) { return o == QLIN_OUT_BF16 ? 2 : 4; }
+
+// Shared checks of the product calls.  variant: qlin::Variant.
+qlin_status check_product(int variant, const void* q_x, const float* s_x, const void* q_w, const uint16_t* s_w,
+                          const void* y, int64_t M, int64_t N, int64_t K, qlin_out out, qlin_path path,
+                          bool* noop) {
+    *noop = false;
+    if (!valid_mn(M) || !valid_mn(N) || !valid_k(K)) return QLIN_ERR_SHAPE;
+    if (variant == qlin::VAR_FP8_BLOCK && ((N % 128) != 0 || (K % 128) != 0)) return QLIN_ERR_SHAPE;
+    if (out != QLIN_OUT_BF16 && out != QLIN_OUT_F32 && out != QLIN_OUT_I32) return QLIN_ERR_UNSUPPORTED;
+    if (out == QLIN_OUT_I32 && variant != qlin::VAR_INT8) return QLIN_ERR_UNSUPPORTED;
+    if (path != QLIN_PATH_AUTO && path != QLIN_PATH_GEMV && path != QLIN_PATH_SMALL && path != QLIN_PATH_LARGE)
+        return QLIN_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return QLIN_OK;
+    }
+    if (path == QLIN_PATH_GEMV && M != 1) return QLIN_ERR_UNSUPPORTED;
+    if (path == QLIN_PATH_SMALL && M > 32) return QLIN_ERR_UNSUPPORTED;
+    if (!q_x || !s_x || !q_w || !s_w || !y) return QLIN_ERR_NULL;
+    if (!aligned(q_x, 16) || !aligned(q_w, 16) || !aligned(y, 16) || !aligned(s_x, 4) || !aligned(s_w, 2))
+        return QLIN_ERR_ALIGN;
+    const int64_t kb = K / 128;
+    const int64_t sx_n = variant == qlin::VAR_FP8_BLOCK ? M * kb : M;
+    const int64_t sw_n = variant == qlin::VAR_FP8_BLOCK ? (N / 128) * kb : N;
+    const Range ry = rng(y, M * N * out_bytes(out));
+    if (overlap(ry, rng(q_x, M * K)) || overlap(ry, rng(q_w, N * K)) || overlap(ry, rng(s_x, sx_n * 4)) ||
+        overlap(ry, rng(s_w, sw_n * 2)))
+        return QLIN_ERR_ALIAS;
+    return QLIN_OK;
+}
+
+qlin_status run_product(int variant, const void* q_x, const float* s_x, const void* q_w, const uint16_t* s_w,
+                        void* y, int64_t M, int64_t N, int64_t K, qlin_out out, qlin_path path,
+                        hipStream_t stream) {
+    bool noop = false;
+    const qlin_status st = check_product(variant, q_x, s_x, q_w, s_w, y, M, N, K, out, path, &noop);
+    if (st != QLIN_OK || noop) return st;
+    const uint8_t* qx = static_cast<const uint8_t*>(q_x);
+    const uint8_t* qw = static_cast<const uint8_t*>(q_w);
+    qlin_path p = path;
+    if (p == QLIN_PATH_AUTO) p = (M == 1) ? QLIN_PATH_GEMV : (M <= 32 ? QLIN_PATH_SMALL : QLIN_PATH_LARGE);
+    hipError_t e;
+    if (p == QLIN_PATH_GEMV) e = qlin::launch_gemv(variant, qx, s_x, qw, s_w, y, N, K, (int)out, stream);
+    else if (p == QLIN_PATH_SMALL) e = qlin::launch_gemm_small(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
+    else e = qlin::launch_gemm_large(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
+    return hip_status(e);
+}
+
+qlin_status check_quant(const uint16_t* x, int64_t M, int64_t K, const void* q, const float* s, int64_t s_count,
+                        bool* noop) {
+    *noop = false;
+    if (!valid_mn(M) || !valid_k(K)) return QLIN_ERR_SHAPE;
+    if (M == 0) {
+        *noop = true;
+        return QLIN_OK;
+    }
+    if (!x || !q || !s) return QLIN_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return QLIN_ERR_ALIGN;
+    const Range rx = rng(x, M * K * 2), rq = rng(q, M * K), rs = rng(s, s_count * 4);
+    if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return QLIN_ERR_ALIAS;
+    return QLIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qlin_status qlin_quant_act_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t stream) {
+    bool noop = false;
+    const qlin_status st = check_quant(x, M, K, q, s, M, &noop);
+    if (st != QLIN_OK || noop) return st;
+    return hip_status(qlin::launch_quant_int8(x, M, K, q, s, stream));
+}
+
+qlin_status qlin_quant_act_fp8(const uint16_t* x, int64_t M, int64_t K, int32_t group, uint8_t* q, float* s,
+                               hipStream_t stream) {
+    if (group != 0 && group != 128) return QLIN_ERR_SHAPE;
+    if (group == 128 && (K % 128) != 0) return QLIN_ERR_SHAPE;
+    bool noop = false;
+    const int64_t s_count = group ? M * (K / 128) : M;
+    const qlin_status st = check_quant(x, M, K, q, s, s_count, &noop);
+    if (st != QLIN_OK || noop) return st;
+    return hip_status(qlin::launch_quant_fp8(x, M, K, group, q, s, stream));
+}
+
+qlin_status qlin_gemv_w8a8(const int8_t* q_x, const float* s_x, const int8_t* q_w, const uint16_t* s_w, void* y,
+                           int64_t N, int64_t K, qlin_out out, hipStream_t stream) {
+    return run_product(qlin::VAR_INT8, q_x, s_x, q_w, s_w, y, 1, N, K, out, QLIN_PATH_GEMV, stream);
+}
+
+qlin_status qlin_gemm_w8a8(const int8_t* q_x, const float* s_x, const int8_t* q_w, const uint16_t* s_w, void* y,
+                           int64_t M, int64_t N, int64_t K, qlin_out out, hipStream_t stream) {
+    return run_product(qlin::VAR_INT8, q_x, s_x, q_w, s_w, y, M, N, K, out, QLIN_PATH_AUTO, stream);
+}
+
+qlin_status qlin_gemm_w8a8_ex(const int8_t* q_x, const float* s_x, const int8_t* q_w, const uint16_t* s_w, void* y,
+                              int64_t M, int64_t N, int64_t K, qlin_out out, qlin_path path, hipStream_t stream) {
+    return run_product(qlin::VAR_INT8, q_x, s_x, q_w, s_w, y, M, N, K, out, path, stream);
+}
+
+qlin_status qlin_gemm_fp8_rowwise(const uint8_t* q_x, const float* s_x, const uint8_t* q_w, const uint16_t* s_w,
+                                  void* y, int64_t M, int64_t N, int64_t K, qlin_out out, hipStream_t stream) {
+    return run_product(qlin::VAR_FP8_ROW, q_x, s_x, q_w, s_w, y, M, N, K, out, QLIN_PATH_AUTO, stream);
+}
+
+qlin_status qlin_gemm_fp8_rowwise_ex(const uint8_t* q_x, const float* s_x, const uint8_t* q_w,
+                                     const uint16_t* s_w, void* y, int64_t M, int64_t N, int64_t K, qlin_out out,
+                                     qlin_path path, hipStream_t stream) {
+    return run_product(qlin::VAR_FP8_ROW, q_x, s_x, q_w, s_w, y, M, N, K, out, path, stream);
+}
+
+qlin_status qlin_gemm_fp8_block(const uint8_t* q_x, const float* s_x, const uint8_t* q_w, const uint16_t* s_w,
+                                void* y, int64_t M, int64_t N, int64_t K, qlin_out out, hipStream_t stream) {
+    return run_product(qlin::VAR_FP8_BLOCK, q_x, s_x, q_w, s_w, y, M, N, K, out, QLIN_PATH_AUTO, stream);
+}
+
+qlin_status qlin_gemm_fp8_block_ex(const uint8_t* q_x, const float* s_x, const uint8_t* q_w, const uint16_t* s_w,
+                                   void* y, int64_t M, int64_t N, int64_t K, qlin_out out, qlin_path path,
+                                   hipStream_t stream) {
+    return run_product(qlin::VAR_FP8_BLOCK, q_x, s_x, q_w, s_w, y, M, N, K, out, path, stream);
+}
+
+const char* qlin_status_string(qlin_status status) {
+    switch (status) {
+        case QLIN_OK: return "QLIN_OK";
+        case QLIN_ERR_NULL: return "QLIN_ERR_NULL: a required pointer is null";
+        case QLIN_ERR_SHAPE: return "QLIN_ERR_SHAPE: invalid M, N, K or group";
+        case QLIN_ERR_ALIGN: return "QLIN_ERR_ALIGN: a pointer misses its required alignment";
+        case QLIN_ERR_UNSUPPORTED: return "QLIN_ERR_UNSUPPORTED: output mode or path not available";
+        case QLIN_ERR_HIP: return "QLIN_ERR_HIP: the HIP runtime rejected the launch";
+        case QLIN_ERR_ALIAS: return "QLIN_ERR_ALIAS: an output overlaps an input";
+    }
+    return "QLIN_ERR_UNKNOWN";
+}
+
+int qlin_abi_version(void) { return QLIN_ABI_VERSION; }
+
+int qlin_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 / E4M3 conversions,
+// wavefront reductions over DPP, MFMA operand types and the scale epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlin {
+
+typedef int   v4i  __attribute__((ext_vector_type(4)));
+typedef int   v8i  __attribute__((ext_vector_type(8)));
+typedef int   v16i __attribute__((ext_vector_type(16)));
+typedef float v4f  __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+enum OutMode : int { OUT_BF16 = 0, OUT_I32 = 1, OUT_F32 = 2 };
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+
+// Exact widening of a bf16 bit pattern (low 16 bits of b) to f32.
+__device__ __forceinline__ float bf16_lo(uint32_t b) { return __uint_as_float(b << 16); }
+// Widening of the high bf16 of a packed pair.
+__device__ __forceinline__ float bf16_hi(uint32_t b) { return __uint_as_float(b & 0xFFFF0000u); }
+
+// f32 -> bf16 with round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// ---------------------------------------------------------------------------
+// OCP E4M3 encode: the caller saturates to [-448, 448] first; the hardware
+// conversion rounds to nearest even.  Packs (a, b) into bytes 0/1 or 2/3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_pack_lo(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+}
+__device__ __forceinline__ uint32_t e4m3_pack_hi(uint32_t old, float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true);
+}
+
+// ---------------------------------------------------------------------------
+// DPP reductions.  Row = 16 lanes.  After row_* every lane of the row holds
+// the row result; wave_* returns the wave-uniform result.
+// Controls: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)dpp_i<0xB1>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x4E>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x141>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x140>((int)v));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = row_max_u32(v);
+    uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ int row_sum_i32(int v) {
+    v += dpp_i<0xB1>(v);
+    v += dpp_i<0x4E>(v);
+    v += dpp_i<0x141>(v);
+    v += dpp_i<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v = row_sum_i32(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ __forceinline__ float row_sum_f32(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = row_sum_f32(v);
+    float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
+}
+
+// ---------------------------------------------------------------------------
+// Scale epilogue: y = fl32(acc) * fl32(s_x * s_w), written as bf16 (RNE),
+// f32, or (int8 schemes) the raw int32 accumulator.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_rowwise_i32acc(void* y, int64_t idx, int acc, float sx,
+                                                     uint32_t sw_bits, int mode) {
+    if (mode == OUT_I32) {
+        static_cast<int*>(y)[idx] = acc;
+        return;
+    }
+    const float sc = sx * bf16_lo(sw_bits);
+    const float v = (float)acc * sc;
+    if (mode == OUT_F32) static_cast<float*>(y)[idx] = v;
+    else static_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
+}
+
+__device__ __forceinline__ void store_f32(void* y, int64_t idx, float v, int mode) {
+    if (mode == OUT_F32) static_cast<float*>(y)[idx] = v;
+    else static_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
+}
+
+// E4M3 pair decode (bytes 0/1 when HI == false, bytes 2/3 when HI == true).
+typedef float v2f __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ v2f e4m3_unpack2(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+}  // namespace qlin

@@ -1,0 +1,28 @@
+// Launchers shared between the kernel files and the C-ABI layer.  All
+// arguments are validated by the caller (qlin_api.hip) before a launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlin {
+
+enum Variant : int { VAR_INT8 = 0, VAR_FP8_ROW = 1, VAR_FP8_BLOCK = 2 };
+
+hipError_t launch_quant_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st);
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int group, uint8_t* q, float* s,
+                            hipStream_t st);
+
+hipError_t launch_gemv(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw, const uint16_t* sw,
+                       void* y, int64_t N, int64_t K, int mode, hipStream_t st);
+hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
+                             const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
+                             hipStream_t st);
+hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
+                             const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
+                             hipStream_t st);
+
+int gemv_rows_per_wave(int64_t N, int64_t K);
+int small_waves_per_tile(int64_t N, int64_t K);
+
+}  // namespace qlin

@@ -1,0 +1,180 @@
+// Dynamic activation quantizers (bf16 -> int8 or OCP E4M3) for gfx950.
+//
+// Per token (W8A8 model card, intro and "Loading"; FP8-dynamic README,
+// "Creation" recipe): one workgroup per row; each thread holds its 16-byte
+// chunks of the row in registers, so the row is read from HBM once.  The
+// absmax is an integer max over the bf16 bit patterns with the sign bit
+// cleared (for non-negative finite floats the bit order is the value order),
+// reduced across the wavefront with DPP and across the four waves via LDS.
+//
+// Per 128-input group (Qwen3 8B FP8 model card, "Loading"): a group is 16
+// lanes x 8 values, i.e. exactly one 16-lane DPP row, so the group absmax is a
+// DPP row reduction with no LDS at all.
+#include "qlin_device.h"
+#include "qlin_internal.h"
+
+namespace qlin {
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantWaves = kQuantThreads / kWave;
+
+__device__ __forceinline__ uint32_t chunk_absmax_bits(const v4u& v) {
+    // max over 8 bf16 magnitudes (bit patterns with the sign cleared)
+    uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
+    uint32_t c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
+    uint32_t m0 = max(a & 0xFFFFu, a >> 16), m1 = max(b & 0xFFFFu, b >> 16);
+    uint32_t m2 = max(c & 0xFFFFu, c >> 16), m3 = max(d & 0xFFFFu, d >> 16);
+    return max(max(m0, m1), max(m2, m3));
+}
+
+// s = fl32(a / Q), inv = fl32(Q / a) (0 for an all-zero row).  Both are IEEE
+// correctly rounded divides (the default for f32 division in HIP).
+template <bool FP8>
+__device__ __forceinline__ void token_scales(uint32_t amax_bits, float& s, float& inv) {
+    const float q = FP8 ? 448.0f : 127.0f;
+    const float a = __uint_as_float(amax_bits << 16);
+    s = a / q;
+    inv = (amax_bits == 0) ? 0.0f : q / a;
+}
+
+__device__ __forceinline__ int8_t q_int8(float x, float inv) {
+    float t = __builtin_rintf(x * inv);             // v_rndne_f32: half to even
+    t = fminf(fmaxf(t, -127.0f), 127.0f);
+    return (int8_t)(int)t;
+}
+
+__device__ __forceinline__ float sat448(float t) { return fminf(fmaxf(t, -448.0f), 448.0f); }
+
+// 8 bf16 (one 16-byte chunk) -> 8 int8 or 8 E4M3 codes (one 8-byte word).
+template <bool FP8>
+__device__ __forceinline__ v2u quant_chunk(const v4u& v, float inv) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[2];
+    if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t lo = e4m3_pack_lo(sat448(bf16_lo(w[2 * i]) * inv), sat448(bf16_hi(w[2 * i]) * inv));
+            o[i] = e4m3_pack_hi(lo, sat448(bf16_lo(w[2 * i + 1]) * inv), sat448(bf16_hi(w[2 * i + 1]) * inv));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t b0 = (uint8_t)q_int8(bf16_lo(w[2 * i]), inv);
+            uint32_t b1 = (uint8_t)q_int8(bf16_hi(w[2 * i]), inv);
+            uint32_t b2 = (uint8_t)q_int8(bf16_lo(w[2 * i + 1]), inv);
+            uint32_t b3 = (uint8_t)q_int8(bf16_hi(w[2 * i + 1]), inv);
+            o[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+    }
+    return v2u{o[0], o[1]};
+}
+
+// One workgroup per token row.  CPT = 16-byte chunks held per thread; the
+// row has K/8 chunks, chunk c is handled by thread c % 256.
+template <int CPT, bool FP8>
+__global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(
+    const uint16_t* __restrict__ x, int64_t K, uint8_t* __restrict__ q, float* __restrict__ s) {
+    __shared__ uint32_t red[kQuantWaves];
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nchunks = (int)(K >> 3);
+    const v4u* xr = reinterpret_cast<const v4u*>(x + m * K);
+
+    v4u v[CPT];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + j * kQuantThreads;
+        v[j] = (c < nchunks) ? __builtin_nontemporal_load(xr + c) : v4u{0, 0, 0, 0};
+        amax = max(amax, chunk_absmax_bits(v[j]));
+    }
+    amax = wave_max_u32(amax);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
+    __syncthreads();
+    amax = max(max(red[0], red[1]), max(red[2], red[3]));
+
+    float sc, inv;
+    token_scales<FP8>(amax, sc, inv);
+    if (tid == 0) s[m] = sc;
+
+    v2u* qr = reinterpret_cast<v2u*>(q + m * K);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + j * kQuantThreads;
+        if (c < nchunks) qr[c] = quant_chunk<FP8>(v[j], inv);
+    }
+}
+
+// Rows longer than 256 * 8 * 16 values: two passes over the row (the second
+// pass re-reads x, normally from L2).
+template <bool FP8>
+__global__ __launch_bounds__(kQuantThreads) void quant_token_loop_kernel(
+    const uint16_t* __restrict__ x, int64_t K, uint8_t* __restrict__ q, float* __restrict__ s) {
+    __shared__ uint32_t red[kQuantWaves];
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nchunks = K >> 3;
+    const v4u* xr = reinterpret_cast<const v4u*>(x + m * K);
+    uint32_t amax = 0;
+    for (int64_t c = tid; c < nchunks; c += kQuantThreads) amax = max(amax, chunk_absmax_bits(xr[c]));
+    amax = wave_max_u32(amax);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
+    __syncthreads();
+    amax = max(max(red[0], red[1]), max(red[2], red[3]));
+    float sc, inv;
+    token_scales<FP8>(amax, sc, inv);
+    if (tid == 0) s[m] = sc;
+    v2u* qr = reinterpret_cast<v2u*>(q + m * K);
+    for (int64_t c = tid; c < nchunks; c += kQuantThreads) qr[c] = quant_chunk<FP8>(xr[c], inv);
+}
+
+// 128-input groups: group g of the flattened [M*K] array is x[128 g, 128 g + 128)
+// (K % 128 == 0 keeps groups inside rows, and s[M][K/128] flattened is s[g]).
+// Each 16-lane DPP row handles one group; 16 groups per workgroup.
+__global__ __launch_bounds__(kQuantThreads) void quant_group128_fp8_kernel(
+    const uint16_t* __restrict__ x, int64_t ngroups, uint8_t* __restrict__ q, float* __restrict__ s) {
+    const int tid = threadIdx.x;
+    const int64_t g = (int64_t)blockIdx.x * (kQuantThreads / 16) + (tid >> 4);
+    if (g >= ngroups) return;                 // whole 16-lane rows leave together
+    const int64_t c = g * 16 + (tid & 15);    // chunk index in the flattened array
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x) + c);
+    const uint32_t amax = row_max_u32(chunk_absmax_bits(v));
+    float sc, inv;
+    token_scales<true>(amax, sc, inv);
+    if ((tid & 15) == 0) s[g] = sc;
+    reinterpret_cast<v2u*>(q)[c] = quant_chunk<true>(v, inv);
+}
+
+template <bool FP8>
+hipError_t launch_token(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, hipStream_t st) {
+    const int64_t chunks = K / 8;
+    const int64_t cpt = (chunks + kQuantThreads - 1) / kQuantThreads;
+    dim3 grid((unsigned)M), block(kQuantThreads);
+    if (cpt <= 1) hipLaunchKernelGGL((quant_token_kernel<1, FP8>), grid, block, 0, st, x, K, q, s);
+    else if (cpt <= 2) hipLaunchKernelGGL((quant_token_kernel<2, FP8>), grid, block, 0, st, x, K, q, s);
+    else if (cpt <= 4) hipLaunchKernelGGL((quant_token_kernel<4, FP8>), grid, block, 0, st, x, K, q, s);
+    else if (cpt <= 8) hipLaunchKernelGGL((quant_token_kernel<8, FP8>), grid, block, 0, st, x, K, q, s);
+    else if (cpt <= 16) hipLaunchKernelGGL((quant_token_kernel<16, FP8>), grid, block, 0, st, x, K, q, s);
+    else hipLaunchKernelGGL((quant_token_loop_kernel<FP8>), grid, block, 0, st, x, K, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st) {
+    return launch_token<false>(x, M, K, reinterpret_cast<uint8_t*>(q), s, st);
+}
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int group, uint8_t* q, float* s,
+                            hipStream_t st) {
+    if (group == 0) return launch_token<true>(x, M, K, q, s, st);
+    const int64_t ngroups = M * (K / 128);
+    const int64_t per_block = kQuantThreads / 16;
+    dim3 grid((unsigned)((ngroups + per_block - 1) / per_block)), block(kQuantThreads);
+    hipLaunchKernelGGL(quant_group128_fp8_kernel, grid, block, 0, st, x, ngroups, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace qlin

@@ -1,0 +1,133 @@
+"""C-ABI boundary checks that run without a GPU: the library loads, exports
+every symbol include/qlin.h declares, and rejects bad arguments from the host
+before any launch (the calls below never reach a kernel: validation returns
+first, so fake device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlin.h")
+
+Q = pytest.importorskip("quantized_linear_layers_token_amd")
+L = Q.lib()
+
+A = 0x10000000          # a fake, 256-byte aligned "device" address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlin_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported by libqlin.so"
+        assert n in Q.SIGNATURES, f"{n} has no binding signature"
+    assert set(Q.SIGNATURES) == set(names)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define QLIN_ABI_VERSION (\d+)", text).group(1)) == Q.ABI_VERSION == L.qlin_abi_version()
+    assert int(re.search(r"#define QLIN_MAX_K\s+(\d+)", text).group(1)) == Q.MAX_K
+    enums = dict((k, int(v)) for k, v in re.findall(r"(QLIN_[A-Z0-9_]+) = (\d+)", text))
+    assert enums["QLIN_OK"] == Q.QLIN_OK and enums["QLIN_ERR_ALIAS"] == Q.QLIN_ERR_ALIAS
+    assert enums["QLIN_OUT_I32"] == Q.OUT_I32 and enums["QLIN_PATH_LARGE"] == Q.PATH_LARGE
+    assert 127 * 128 * Q.MAX_K < 2 ** 31
+
+
+def test_status_strings():
+    for s in range(7):
+        assert Q.status_string(s).startswith("QLIN_")
+    assert Q.status_string(99) == "QLIN_ERR_UNKNOWN"
+    assert L.qlin_last_hip_error() == 0
+
+
+def quant_int8(x, M, K, q, s):
+    return L.qlin_quant_act_int8(x, M, K, q, s, None)
+
+
+def gemm(fn, qx, sx, qw, sw, y, M, N, K, out=0, path=0):
+    return getattr(L, fn + "_ex")(qx, sx, qw, sw, y, M, N, K, out, path, None)
+
+
+B = {"qx": A, "sx": A + 0x1000000, "qw": A + 0x2000000, "sw": A + 0x3000000, "y": A + 0x4000000}
+
+
+def test_quant_validation():
+    assert quant_int8(None, 0, 16, None, None) == Q.QLIN_OK                      # M == 0: no-op
+    assert quant_int8(None, 4, 16, None, None) == Q.QLIN_ERR_NULL
+    assert quant_int8(A, 4, 0, A + 4096, A + 8192) == Q.QLIN_ERR_SHAPE
+    assert quant_int8(A, 4, 24, A + 4096, A + 8192) == Q.QLIN_ERR_SHAPE           # K % 16
+    assert quant_int8(A, 4, Q.MAX_K + 16, A + 2 ** 22, A + 2 ** 23) == Q.QLIN_ERR_SHAPE
+    assert quant_int8(A, -1, 16, A + 4096, A + 8192) == Q.QLIN_ERR_SHAPE
+    assert quant_int8(A + 8, 4, 16, A + 4096, A + 8192) == Q.QLIN_ERR_ALIGN
+    assert quant_int8(A, 4, 16, A + 4096 + 4, A + 8192) == Q.QLIN_ERR_ALIGN
+    assert quant_int8(A, 4, 16, A + 4096, A + 8192 + 2) == Q.QLIN_ERR_ALIGN
+    assert quant_int8(A, 4, 16, A + 64, A + 8192) == Q.QLIN_ERR_ALIAS            # q inside x (128 bytes)
+    assert quant_int8(A, 4, 16, A + 4096, A + 4096 + 32) == Q.QLIN_ERR_ALIAS     # s inside q
+    f8 = L.qlin_quant_act_fp8
+    assert f8(A, 4, 16, 64, A + 4096, A + 8192, None) == Q.QLIN_ERR_SHAPE          # group must be 0 / 128
+    assert f8(A, 4, 144, 128, A + 4096, A + 8192, None) == Q.QLIN_ERR_SHAPE        # K % 128 for groups
+    assert f8(None, 0, 128, 128, None, None, None) == Q.QLIN_OK
+
+
+@pytest.mark.parametrize("fn", ["qlin_gemm_w8a8", "qlin_gemm_fp8_rowwise", "qlin_gemm_fp8_block"])
+def test_product_validation(fn):
+    b = B
+    args = (b["qx"], b["sx"], b["qw"], b["sw"], b["y"])
+    assert gemm(fn, *args, 0, 256, 256) == Q.QLIN_OK                     # M == 0
+    assert gemm(fn, *args, 4, 0, 256) == Q.QLIN_OK                       # N == 0
+    assert gemm(fn, None, *args[1:], 4, 256, 256) == Q.QLIN_ERR_NULL
+    assert gemm(fn, *args[:4], None, 4, 256, 256) == Q.QLIN_ERR_NULL
+    assert gemm(fn, *args, 4, 256, 0) == Q.QLIN_ERR_SHAPE
+    assert gemm(fn, *args, 4, 256, 40) == Q.QLIN_ERR_SHAPE
+    assert gemm(fn, *args, 4, -256, 256) == Q.QLIN_ERR_SHAPE
+    assert gemm(fn, b["qx"] + 8, *args[1:], 4, 256, 256) == Q.QLIN_ERR_ALIGN
+    assert gemm(fn, *args[:2], b["qw"] + 4, *args[3:], 4, 256, 256) == Q.QLIN_ERR_ALIGN
+    assert gemm(fn, *args[:4], b["y"] + 2, 4, 256, 256) == Q.QLIN_ERR_ALIGN
+    assert gemm(fn, *args[:3], b["sw"] + 1, b["y"], 4, 256, 256) == Q.QLIN_ERR_ALIGN
+    assert gemm(fn, *args, 4, 256, 256, out=7) == Q.QLIN_ERR_UNSUPPORTED
+    assert gemm(fn, *args, 4, 256, 256, path=9) == Q.QLIN_ERR_UNSUPPORTED
+    assert gemm(fn, *args, 2, 256, 256, path=Q.PATH_GEMV) == Q.QLIN_ERR_UNSUPPORTED
+    assert gemm(fn, *args, 33, 256, 256, path=Q.PATH_SMALL) == Q.QLIN_ERR_UNSUPPORTED
+    assert gemm(fn, *args[:4], b["qw"] + 256, 4, 256, 256) == Q.QLIN_ERR_ALIAS    # y overlaps q_w
+    if fn == "qlin_gemm_w8a8":
+        pass
+    else:
+        assert gemm(fn, *args, 4, 256, 256, out=Q.OUT_I32) == Q.QLIN_ERR_UNSUPPORTED
+    if fn == "qlin_gemm_fp8_block":
+        assert gemm(fn, *args, 4, 200, 256) == Q.QLIN_ERR_SHAPE           # N % 128
+        assert gemm(fn, *args, 4, 256, 272) == Q.QLIN_ERR_SHAPE           # K % 128
+
+
+def test_gemv_validation():
+    b = B
+    g = L.qlin_gemv_w8a8
+    assert g(b["qx"], b["sx"], b["qw"], b["sw"], b["y"], 0, 256, 0, None) == Q.QLIN_OK
+    assert g(None, b["sx"], b["qw"], b["sw"], b["y"], 16, 256, 0, None) == Q.QLIN_ERR_NULL
+    assert g(b["qx"], b["sx"], b["qw"], b["sw"], b["y"], 16, 100, 0, None) == Q.QLIN_ERR_SHAPE
+    assert g(b["qx"], b["sx"], b["qw"], b["sw"], b["y"], 16, 256, 5, None) == Q.QLIN_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    # The package's loader raises when the shared library is absent (no fallback).
+    import importlib.util
+    src = os.path.join(ROOT, "quantized_linear_layers_token_amd", "__init__.py")
+    pkg = tmp_path / "qlin_copy"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("qlin_copy", str(pkg / "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="no fallback"):
+        spec.loader.exec_module(mod)
+
+
+def test_ctypes_handle_is_shared():
+    assert isinstance(L, ctypes.CDLL)
