@@ -55,9 +55,11 @@ class Launcher:
     """Pre-marshalled C-ABI calls (raw pointers), so a step is a list of calls."""
 
     def __init__(self, Q, torch):
+        self.Q = Q
         self.L = Q.lib()
         self.torch = torch
         self.calls = []
+        self.keep = []
 
     def stream(self):
         return self.torch.cuda.current_stream().cuda_stream
@@ -69,6 +71,15 @@ class Launcher:
     def quant_fp8(self, x, q, s, group):
         M, K = x.shape
         self.calls.append((self.L.qlin_quant_act_fp8, (x.data_ptr(), M, K, group, q.data_ptr(), s.data_ptr())))
+
+    def linear(self, scheme, x, segs, out=0, qx=None, sx=None):
+        """segs: [(q_w, s_w, y), ...] sharing x."""
+        M, K = x.shape
+        arr = self.Q.segments_array(segs)
+        self.keep.append(arr)
+        self.calls.append((self.L.qlin_linear, (scheme, x.data_ptr(), M, K, arr, len(segs), out,
+                                                 None if qx is None else qx.data_ptr(),
+                                                 None if sx is None else sx.data_ptr())))
 
     def gemm(self, fn, qx, sx, qw, sw, y, M, N, K, out=0, path=0):
         f = getattr(self.L, fn + "_ex")
@@ -128,15 +139,26 @@ def quant_bytes(M, K):
     return 2 * M * K + M * K + 4 * M
 
 
+def fused_bytes(K, ns):
+    """Algorithmic bytes of one fused projection call at M = 1: the bf16 input
+    row once, every weight byte once, the row scales, the bf16 outputs."""
+    return 2 * K + sum(N * K + 2 * N + 2 * N for N in ns)
+
+
 def build_decode(torch, Q, W, layers, dev):
-    """32 layers of int8 projections with distinct weights + per-layer inputs."""
+    """32 layers of int8 projections with distinct weights + per-layer inputs.
+    F: the fused step (one qlin_linear launch per layer input: q/k/v, o,
+    gate/up, down); L: the two-kernel step (quantizer + one-row product per
+    projection); G: the one-row products alone."""
+    F = Launcher(Q, torch)
     L = Launcher(Q, torch)
-    G = Launcher(Q, torch)          # products only (for the roofline)
+    G = Launcher(Q, torch)
     gen = torch.Generator(device=dev)
     shapes = dict((n, (N, K)) for n, N, K in W.LLAMA_8B)
     bufs = []
     step_bytes = 0
     gemv_bytes = 0
+    fused_step_bytes = 0
     per_shape = {}
     for layer in range(layers):
         gen.manual_seed(100 + layer)
@@ -154,6 +176,8 @@ def build_decode(torch, Q, W, layers, dev):
             L.quant_int8(x, q, s)
             step_bytes += quant_bytes(1, K)
             lw["in_" + group[0]] = (x, q, s)
+            F.linear(0, x, [(lw[name][0], lw[name][1], lw[name][2]) for name in group])
+            fused_step_bytes += fused_bytes(K, [shapes[name][0] for name in group])
             for name in group:
                 qw, sw, y = lw[name]
                 N, K2 = shapes[name]
@@ -164,7 +188,7 @@ def build_decode(torch, Q, W, layers, dev):
                 gemv_bytes += b
                 per_shape.setdefault(name, []).append((q, s, qw, sw, y, N, K2))
         bufs.append(lw)
-    return L, G, bufs, step_bytes, gemv_bytes, per_shape
+    return F, L, G, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape
 
 
 def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
@@ -225,7 +249,6 @@ def cpu_baseline(torch, W, bufs, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    shapes = dict((n, (N, K)) for n, N, K in W.LLAMA_8B)
     t_total = 0.0
     nbytes = 0
     nproj = 0
@@ -235,17 +258,21 @@ def cpu_baseline(torch, W, bufs, budget_s):
     for lw in bufs:
         for group in W.INPUT_GROUPS:
             x = lw["in_" + group[0]][0].cpu().numpy().view(np.uint16)
+            ws = []
             for name in group:
                 qw_t, sw_t, y_t = lw[name]
-                qw = qw_t.cpu().numpy()
-                sw = sw_t.cpu().numpy().view(np.uint16)
-                N, K = shapes[name]
-                t0 = time.perf_counter()
-                yb, y_exact, qx, sx, acc = O.linear_w8a8(x, qw, sw)
-                t_total += time.perf_counter() - t0
-                nbytes += decode_bytes(N, K)
+                ws.append((qw_t.cpu().numpy(), sw_t.cpu().numpy().view(np.uint16), y_t.cpu().numpy().view(np.uint16)))
+            t0 = time.perf_counter()
+            qx, sx = O.quant_act_int8(x)                       # one rounding per layer input
+            outs = []
+            for qw, sw, _ in ws:
+                acc = O.contract_int8(qx, qw)
+                outs.append((acc, O.rescale_rowwise(acc, sx, sw)))
+            t_total += time.perf_counter() - t0
+            K = x.shape[1]
+            nbytes += fused_bytes(K, [qw.shape[0] for qw, _, _ in ws])
+            for (qw, sw, yg), (acc, y_exact) in zip(ws, outs):
                 nproj += 1
-                yg = y_t.cpu().numpy().view(np.uint16)
                 yf = (yg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
                 max_rel = max(max_rel, float(np.max(np.abs(yf - y_exact)) / np.max(np.abs(y_exact))))
                 exact_order &= bool(np.array_equal(yg, O.epilogue_f32_order(acc, sx, sw)))
@@ -282,9 +309,10 @@ def main():
 
     # ---- headline: decode, M = 1, 32 distinct layers -------------------------
     log("building decode workload (32 layers, int8)")
-    L, G, bufs, step_bytes, gemv_bytes, per_shape = build_decode(torch, Q, W, W.LLAMA_8B_LAYERS, dev)
+    F, L, G, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape = build_decode(
+        torch, Q, W, W.LLAMA_8B_LAYERS, dev)
     torch.cuda.synchronize()
-    step = capture(torch, L.run, use_graph)
+    step = capture(torch, F.run, use_graph)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -293,26 +321,36 @@ def main():
     ms = time_events(torch, step, args.steps)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    value = step_bytes / (ms * 1e-3) / 1e9
+    value = fused_step_bytes / (ms * 1e-3) / 1e9
     log(f"decode step {ms:.4f} ms (wall {wall_ms:.4f} ms)  {value:.1f} GB/s")
 
-    # ---- roofline of the dominant kernel: the int8 one-row product ----------
-    gemv_only = capture(torch, G.run, use_graph)
-    for _ in range(2):
-        gemv_only()
-    n_launch = len(G.calls)
-    ms_gemv = time_events(torch, gemv_only, max(3, args.steps // 2))
-    avg_launch_us = ms_gemv * 1e3 / n_launch
-    bytes_per_launch = gemv_bytes / n_launch
+    # ---- roofline of the dominant kernel: the fused one-row projection -----
+    # (the step is made of these launches only: avg launch = step time / 128)
+    n_launch = len(F.calls)
+    ms_f = time_events(torch, step, max(3, args.steps // 2))
+    avg_launch_us = ms_f * 1e3 / n_launch
+    bytes_per_launch = fused_step_bytes / n_launch
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemv_kernel<VAR_INT8,...> (qlin_gemm_w8a8 at M=1)",
+                "kernel": "linear_decode_kernel<VAR_INT8,...> (qlin_linear, M=1)",
                 "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 3),
                 "launches": n_launch}
-    log(f"gemv-only: {n_launch} launches, avg {avg_launch_us:.3f} us, {achieved:.1f} GB/s")
+    log(f"fused launches: {n_launch}, avg {avg_launch_us:.3f} us, {achieved:.1f} GB/s")
 
     secondary = {}
+    # the two-kernel form of the same step (quantizer + one-row product per projection)
+    two = capture(torch, L.run, use_graph)
+    two()
+    ms_two = time_events(torch, two, max(3, args.steps // 2))
+    gemv_only = capture(torch, G.run, use_graph)
+    gemv_only()
+    ms_gemv = time_events(torch, gemv_only, max(3, args.steps // 2))
+    secondary["decode_two_kernel"] = {
+        "ms_per_step": round(ms_two, 4), "gbs": round(step_bytes / (ms_two * 1e-3) / 1e9, 1),
+        "gemv_only_gbs": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
+        "gemv_avg_launch_us": round(ms_gemv * 1e3 / len(G.calls), 3)}
+    log(f"two-kernel step {ms_two:.4f} ms; gemv-only {secondary['decode_two_kernel']}")
     if not args.quick:
         # per-shape one-row bandwidth (all 32 layers of one projection back to back)
         shape_gbs = {}
@@ -405,10 +443,11 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "Llama-3.1-8B W8A8 decode, M=1, 32 layers with distinct int8 weights; per token 128 "
-                        "per-token int8 activation quantizations + 224 one-row products (q, k, v, o, gate, up, "
-                        "down), " + ("replayed as one HIP graph" if use_graph else "launched eagerly"),
-            "bytes_per_step": step_bytes,
+            "workload": "Llama-3.1-8B W8A8 decode, M=1, 32 layers with distinct int8 weights (q, k, v, o, gate, "
+                        "up, down as separate tensors); per token 128 fused launches (per-token int8 activation "
+                        "rounding + one-row products of the projections reading that input), " +
+                        ("replayed as one HIP graph" if use_graph else "launched eagerly"),
+            "bytes_per_step": fused_step_bytes,
             "hip_graph": use_graph,
         },
         "roofline": roofline,

@@ -168,6 +168,47 @@ qlin_status qlin_gemm_fp8_block_ex(const uint8_t* q_x, const float* s_x,
                                    qlin_path path, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Fused projection: bf16 activations in                                  */
+/* ---------------------------------------------------------------------- */
+
+typedef enum qlin_scheme {
+    QLIN_SCHEME_W8A8 = 0,         /* int8 per-token activations, int8 weights, bf16 row scales */
+    QLIN_SCHEME_FP8_ROWWISE = 1,  /* E4M3 per-token activations, E4M3 weights, bf16 row scales */
+    QLIN_SCHEME_FP8_BLOCK = 2     /* E4M3 1x128-group activations, E4M3 weights, bf16 128x128 block scales */
+} qlin_scheme;
+
+#define QLIN_MAX_SEGMENTS 4
+
+/* One weight matrix reading the call's activations.  q_w [n, K] (int8 or E4M3
+ * codes), s_w bf16 [n] (rowwise schemes) or [n/128, K/128] (block scheme; n % 128
+ * == 0), y [M, n] in the call's output mode.  Host struct; pointers are device
+ * memory. */
+typedef struct qlin_segment {
+    const void* q_w;
+    const uint16_t* s_w;
+    void* y;
+    int64_t n;
+} qlin_segment;
+
+/* Quantize the bf16 activations x [M, K] with the scheme's dynamic rounding and
+ * multiply them by each of the nseg (1..QLIN_MAX_SEGMENTS) weight segments:
+ * segments[i].y = product of x with segments[i] (the definition of
+ * qlin_gemm_w8a8 / qlin_gemm_fp8_rowwise / qlin_gemm_fp8_block applied to the
+ * codes and scales of qlin_quant_act_int8 / qlin_quant_act_fp8).  Projections
+ * that read the same layer input (q/k/v, gate/up) share one rounding of it
+ * (W8A8 model card, intro and "Loading"; Qwen3 8B FP8 card, "Loading").
+ *
+ * M == 1 and K <= 16384: one launch -- every workgroup rounds the row into LDS
+ * and streams its share of all segments' weight rows; q_x / s_x may be null, and
+ * when given receive the codes and scale(s).  Otherwise q_x (M*K bytes) and s_x
+ * ([M] or [M, K/128] f32) are required caller-owned staging buffers: one
+ * quantizer launch, then one product launch per segment (regime by M).
+ * The segments array is read during the call only. */
+qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                        const qlin_segment* segments, int32_t nseg, qlin_out out,
+                        void* q_x, float* s_x, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Helpers                                                                */
 /* ---------------------------------------------------------------------- */
 

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libqlin.so")
 
 QLIN_OK, QLIN_ERR_NULL, QLIN_ERR_SHAPE, QLIN_ERR_ALIGN, QLIN_ERR_UNSUPPORTED, QLIN_ERR_HIP, QLIN_ERR_ALIAS = range(7)
 OUT_BF16, OUT_I32, OUT_F32 = 0, 1, 2
+SCHEME_W8A8, SCHEME_FP8_ROWWISE, SCHEME_FP8_BLOCK = 0, 1, 2
+MAX_SEGMENTS = 4
 PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_LARGE = 0, 1, 2, 3
 ABI_VERSION = 1
 MAX_K = 131072
@@ -35,10 +37,16 @@ SIGNATURES = {
     "qlin_gemm_fp8_rowwise_ex": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _S, _P]),
     "qlin_gemm_fp8_block": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _P]),
     "qlin_gemm_fp8_block_ex": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _S, _P]),
+    "qlin_linear": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P, _P, _P]),
     "qlin_status_string": (ctypes.c_char_p, [_S]),
     "qlin_abi_version": (_S, []),
     "qlin_last_hip_error": (_S, []),
 }
+
+
+class QlinSegment(ctypes.Structure):
+    """struct qlin_segment: one weight matrix reading the call's activations."""
+    _fields_ = [("q_w", ctypes.c_void_p), ("s_w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class QlinError(RuntimeError):
@@ -156,3 +164,27 @@ def qlin_gemm_fp8_block(q_x, s_x, q_w, s_w, y, out=OUT_BF16, path=PATH_AUTO, str
 
 def status_string(status: int) -> str:
     return _lib.qlin_status_string(status).decode()
+
+
+# --------------------------------------------------------------------------
+# Fused projection (bf16 activations in)
+# --------------------------------------------------------------------------
+
+def segments_array(segments):
+    """[(q_w [n, K], s_w, y), ...] -> ctypes array of QlinSegment."""
+    arr = (QlinSegment * len(segments))()
+    for i, (qw, sw, y) in enumerate(segments):
+        arr[i] = QlinSegment(_ptr(qw), _ptr(sw), _ptr(y), qw.shape[0])
+    return arr
+
+
+def qlin_linear(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=None):
+    """x bf16 [M, K]; segments: list of (q_w [n, K], s_w, y [M, n]) sharing x.
+    q_x / s_x: staging for the quantized activations (optional at M == 1)."""
+    M, K = _dims2(x, "x")
+    for qw, _, _ in segments:
+        if qw.dim() != 2 or qw.shape[1] != K:
+            raise ValueError("every q_w must be [n, K]")
+    arr = segments_array(segments)
+    _check(_lib.qlin_linear(scheme, _ptr(x), M, K, arr, len(segments), out, _ptr(q_x), _ptr(s_x),
+                            _stream(stream)), "qlin_linear")

@@ -55,28 +55,28 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ sw,
     void* __restrict__ y, int N, int K, int mode) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6)) * R;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform row bookkeeping
+    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * R;
     if (n0 >= N) return;                       // the whole wave leaves together
 
     const int k16 = K >> 4;                    // 16-byte slices per row
+    // Weights first, branch-free: slices past K re-read the row's last slice
+    // and meet zero activation slices; tail rows re-read the last row (not stored).
+    v4u wr[R][KC];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = min(n0 + r, (int64_t)N - 1);
+        const v4u* wrow = reinterpret_cast<const v4u*>(qw + n * K);
+#pragma unroll
+        for (int j = 0; j < KC; ++j) wr[r][j] = __builtin_nontemporal_load(wrow + min(j * kWave + lane, k16 - 1));
+    }
     const v4u* xv = reinterpret_cast<const v4u*>(qx);
     v4u xr[KC];
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
         const int o = j * kWave + lane;
-        xr[j] = (o < k16) ? xv[o] : v4u{0, 0, 0, 0};
-    }
-
-    v4u wr[R][KC];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t n = min(n0 + r, (int64_t)N - 1);   // tail rows re-read the last row; not stored
-        const v4u* wrow = reinterpret_cast<const v4u*>(qw + n * K);
-#pragma unroll
-        for (int j = 0; j < KC; ++j) {
-            const int o = j * kWave + lane;
-            wr[r][j] = (o < k16) ? __builtin_nontemporal_load(wrow + o) : v4u{0, 0, 0, 0};
-        }
+        const v4u v = xv[min(o, k16 - 1)];
+        xr[j] = (o < k16) ? v : v4u{0, 0, 0, 0};
     }
 
     if constexpr (V == VAR_INT8) {
@@ -106,12 +106,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 const uint16_t* swr = sw + (n >> 7) * kbs;
 #pragma unroll
                 for (int j = 0; j < KC; ++j) {
-                    const int o = j * kWave + lane;
-                    if (o < k16) {
-                        const int kb = o >> 3;  // 8 slices of 16 bytes per 128-wide block
-                        const float f = sx[kb] * bf16_lo(swr[kb]);
-                        a = __builtin_fmaf(dot16_e4m3(wr[r][j], xr[j]), f, a);
-                    }
+                    const int kb = min(j * kWave + lane, k16 - 1) >> 3;  // 8 slices of 16 bytes per block
+                    const float f = sx[kb] * bf16_lo(swr[kb]);
+                    a = __builtin_fmaf(dot16_e4m3(wr[r][j], xr[j]), f, a);
                 }
             } else {
 #pragma unroll
@@ -143,7 +140,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_loop_kernel(
     void* __restrict__ y, int N, int K, int mode) {
     constexpr int KC = 16;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6)) * R;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * R;
     if (n0 >= N) return;
     const int k16 = K >> 4;
     const int kbs = K >> 7;

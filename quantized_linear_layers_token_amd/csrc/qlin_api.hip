@@ -95,9 +95,97 @@ qlin_status check_quant(const uint16_t* x, int64_t M, int64_t K, const void* q, 
     return QLIN_OK;
 }
 
+qlin_status check_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segs,
+                         int32_t nseg, qlin_out out, const void* q_x, const float* s_x, bool fused, bool* noop) {
+    *noop = false;
+    if (scheme != QLIN_SCHEME_W8A8 && scheme != QLIN_SCHEME_FP8_ROWWISE && scheme != QLIN_SCHEME_FP8_BLOCK)
+        return QLIN_ERR_UNSUPPORTED;
+    if (!segs) return QLIN_ERR_NULL;
+    if (nseg < 1 || nseg > QLIN_MAX_SEGMENTS) return QLIN_ERR_SHAPE;
+    if (!valid_mn(M) || !valid_k(K)) return QLIN_ERR_SHAPE;
+    const bool block = scheme == QLIN_SCHEME_FP8_BLOCK;
+    if (block && (K % 128) != 0) return QLIN_ERR_SHAPE;
+    if (out != QLIN_OUT_BF16 && out != QLIN_OUT_F32 && out != QLIN_OUT_I32) return QLIN_ERR_UNSUPPORTED;
+    if (out == QLIN_OUT_I32 && scheme != QLIN_SCHEME_W8A8) return QLIN_ERR_UNSUPPORTED;
+    int64_t ntot = 0;
+    for (int i = 0; i < nseg; ++i) {
+        if (!valid_mn(segs[i].n)) return QLIN_ERR_SHAPE;
+        if (block && (segs[i].n % 128) != 0) return QLIN_ERR_SHAPE;
+        ntot += segs[i].n;
+    }
+    if (ntot > QLIN_MAX_MN) return QLIN_ERR_SHAPE;
+    if (M == 0 || ntot == 0) {
+        *noop = true;
+        return QLIN_OK;
+    }
+    if (!x) return QLIN_ERR_NULL;
+    if (!fused && (!q_x || !s_x)) return QLIN_ERR_NULL;
+    if ((q_x == nullptr) != (s_x == nullptr)) return QLIN_ERR_NULL;
+    if (!aligned(x, 16) || (q_x && !aligned(q_x, 16)) || (s_x && !aligned(s_x, 4))) return QLIN_ERR_ALIGN;
+    const int64_t sx_n = block ? M * (K / 128) : M;
+    const Range rx = rng(x, M * K * 2);
+    Range rq = rng(q_x, q_x ? M * K : 0), rs = rng(s_x, s_x ? sx_n * 4 : 0);
+    if (q_x && (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs))) return QLIN_ERR_ALIAS;
+    for (int i = 0; i < nseg; ++i) {
+        if (segs[i].n == 0) continue;
+        if (!segs[i].q_w || !segs[i].s_w || !segs[i].y) return QLIN_ERR_NULL;
+        if (!aligned(segs[i].q_w, 16) || !aligned(segs[i].y, 16) || !aligned(segs[i].s_w, 2)) return QLIN_ERR_ALIGN;
+        const Range ry = rng(segs[i].y, M * segs[i].n * out_bytes(out));
+        if (overlap(ry, rx) || (q_x && (overlap(ry, rq) || overlap(ry, rs)))) return QLIN_ERR_ALIAS;
+        for (int j = 0; j < nseg; ++j) {
+            if (segs[j].n == 0) continue;
+            const int64_t swn = block ? (segs[j].n / 128) * (K / 128) : segs[j].n;
+            if (overlap(ry, rng(segs[j].q_w, segs[j].n * K)) || overlap(ry, rng(segs[j].s_w, swn * 2)))
+                return QLIN_ERR_ALIAS;
+            if (j != i && overlap(ry, rng(segs[j].y, M * segs[j].n * out_bytes(out)))) return QLIN_ERR_ALIAS;
+        }
+    }
+    return QLIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
+                        int32_t nseg, qlin_out out, void* q_x, float* s_x, hipStream_t stream) {
+    const bool fused = (M == 1) && (K <= qlin::kDecodeMaxK);
+    bool noop = false;
+    const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, q_x, s_x, fused, &noop);
+    if (st != QLIN_OK || noop) return st;
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
+                        : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
+    if (fused) {
+        qlin::SegmentArgs sa{};
+        int n = 0, k = 0;
+        for (int i = 0; i < nseg; ++i) {
+            if (segments[i].n == 0) continue;
+            sa.w[k] = static_cast<const uint8_t*>(segments[i].q_w);
+            sa.sw[k] = segments[i].s_w;
+            sa.y[k] = segments[i].y;
+            sa.start[k] = n;
+            n += (int)segments[i].n;
+            ++k;
+        }
+        sa.nseg = k;
+        for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
+        return hip_status(qlin::launch_linear_decode(variant, x, K, sa, (int)out, static_cast<uint8_t*>(q_x), s_x,
+                                                     stream));
+    }
+    hipError_t e;
+    if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);
+    else e = qlin::launch_quant_fp8(x, M, K, variant == qlin::VAR_FP8_BLOCK ? 128 : 0, static_cast<uint8_t*>(q_x),
+                                    s_x, stream);
+    if (e != hipSuccess) return hip_status(e);
+    for (int i = 0; i < nseg; ++i) {
+        if (segments[i].n == 0) continue;
+        const qlin_status s = run_product(variant, q_x, s_x, segments[i].q_w, segments[i].s_w, segments[i].y, M,
+                                          segments[i].n, K, out, QLIN_PATH_AUTO, stream);
+        if (s != QLIN_OK) return s;
+    }
+    return QLIN_OK;
+}
+
 
 qlin_status qlin_quant_act_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t stream) {
     bool noop = false;

@@ -9,6 +9,17 @@ namespace qlin {
 
 enum Variant : int { VAR_INT8 = 0, VAR_FP8_ROW = 1, VAR_FP8_BLOCK = 2 };
 
+// Weight segments that read the same activation row (e.g. q, k, v): rows of
+// segment i are global rows [start[i], start[i+1]).  Passed by value.
+constexpr int kMaxSegments = 4;
+struct SegmentArgs {
+    const uint8_t* w[kMaxSegments];
+    const uint16_t* sw[kMaxSegments];
+    void* y[kMaxSegments];
+    int start[kMaxSegments + 1];
+    int nseg;
+};
+
 hipError_t launch_quant_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st);
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int group, uint8_t* q, float* s,
                             hipStream_t st);
@@ -21,6 +32,10 @@ hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, co
 hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
                              const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
                              hipStream_t st);
+
+hipError_t launch_linear_decode(int variant, const uint16_t* x, int64_t K, const SegmentArgs& sa, int mode,
+                                uint8_t* qx, float* sx, hipStream_t st);
+constexpr int64_t kDecodeMaxK = 16384;   // fused one-row path keeps the quantized row in LDS/registers
 
 int gemv_rows_per_wave(int64_t N, int64_t K);
 int small_waves_per_tile(int64_t N, int64_t K);

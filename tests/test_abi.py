@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libqlin.so"
         assert n in Q.SIGNATURES, f"{n} has no binding signature"
@@ -131,3 +131,33 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 def test_ctypes_handle_is_shared():
     assert isinstance(L, ctypes.CDLL)
+
+
+def test_linear_validation():
+    Seg = Q.QlinSegment
+    x = A
+    segs = (Seg * 3)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 64),
+                     Seg(A + 0x4000000, A + 0x5000000, A + 0x6000000, 64),
+                     Seg(A + 0x7000000, A + 0x8000000, A + 0x9000000, 128))
+    lin = L.qlin_linear
+    assert lin(0, x, 1, 256, None, 1, 0, None, None, None) == Q.QLIN_ERR_NULL
+    assert lin(0, x, 1, 256, segs, 0, 0, None, None, None) == Q.QLIN_ERR_SHAPE
+    assert lin(0, x, 1, 256, segs, 5, 0, None, None, None) == Q.QLIN_ERR_SHAPE
+    assert lin(9, x, 1, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_UNSUPPORTED
+    assert lin(1, x, 1, 256, segs, 3, Q.OUT_I32, None, None, None) == Q.QLIN_ERR_UNSUPPORTED
+    assert lin(2, x, 1, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_SHAPE       # block: n % 128
+    assert lin(0, x, 0, 256, segs, 3, 0, None, None, None) == Q.QLIN_OK              # M == 0
+    assert lin(0, x, 1, 250, segs, 3, 0, None, None, None) == Q.QLIN_ERR_SHAPE
+    assert lin(0, None, 1, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_NULL
+    assert lin(0, x, 4, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_NULL         # M > 1 needs staging
+    assert lin(0, x, 4, 256, segs, 3, 0, A + 0xA000000, None, None) == Q.QLIN_ERR_NULL
+    assert lin(0, x + 8, 1, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_ALIGN
+    bad = (Seg * 2)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 64),
+                    Seg(A + 0x4000000, A + 0x5000000, A + 0x3000000 + 64, 64))    # outputs overlap
+    assert lin(0, x, 1, 256, bad, 2, 0, None, None, None) == Q.QLIN_ERR_ALIAS
+    bad2 = (Seg * 1)(Seg(A + 0x1000000, A + 0x2000000, A + 0x1000000 + 512, 64))  # y inside q_w
+    assert lin(0, x, 1, 256, bad2, 1, 0, None, None, None) == Q.QLIN_ERR_ALIAS
+    nul = (Seg * 1)(Seg(None, A + 0x2000000, A + 0x3000000, 64))
+    assert lin(0, x, 1, 256, nul, 1, 0, None, None, None) == Q.QLIN_ERR_NULL
+    empty = (Seg * 1)(Seg(None, None, None, 0))
+    assert lin(0, x, 1, 256, empty, 1, 0, None, None, None) == Q.QLIN_OK             # no rows: no-op

@@ -1,0 +1,136 @@
+"""GPU parity of the fused projection (qlin_linear: bf16 activations in) against
+the CPU oracle, for the three schemes, one to four weight segments sharing one
+input, the one-launch path (M = 1) and the staged path (M > 1 or long K)."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_helpers import assert_within_tol, dev, e4m3_equal_mod_zero, empty, host, torch_mod
+
+pytestmark = pytest.mark.gpu
+BF16, I32, F32 = 0, 1, 2
+W8A8, FP8R, FP8B = 0, 1, 2
+
+
+def Q():
+    import quantized_linear_layers_token_amd as q
+    return q
+
+
+def make_segments(scheme, seed, ns, K):
+    segs = []
+    for i, n in enumerate(ns):
+        if scheme == W8A8:
+            qw = W.w_int8(seed + 10 * i, n, K)
+        else:
+            qw = W.w_e4m3(seed + 10 * i, n, K)
+        sw = W.scale_bf16(seed + 10 * i + 1, (n // 128, K // 128) if scheme == FP8B else (n,))
+        segs.append((qw, sw))
+    return segs
+
+
+def run_linear(scheme, x, segs, out, staged):
+    torch = torch_mod()
+    M, K = x.shape
+    esz = 2 if out == BF16 else 4
+    ys = [empty(torch, (M * qw.shape[0] * esz + 64,), torch.uint8, fill=0xFF) for qw, _ in segs]
+    dsegs = [(dev(qw), dev(sw), y) for (qw, sw), y in zip(segs, ys)]
+    qx = sx = None
+    if staged or M > 1:
+        qx = empty(torch, (M, K), torch.uint8, fill=0x55)
+        sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32, fill=0x55)
+    Q().qlin_linear(scheme, dev(x), dsegs, out=out, q_x=qx, s_x=sx)
+    res = []
+    for (qw, _), y in zip(segs, ys):
+        raw = host(y)
+        n = qw.shape[0]
+        assert (raw[M * n * esz:] == 0xFF).all(), "guard band overwritten"
+        body = raw[:M * n * esz]
+        res.append(body.view({BF16: np.uint16, I32: np.int32, F32: np.float32}[out]).reshape(M, n))
+    return res, (None if qx is None else host(qx)), (None if sx is None else host(sx))
+
+
+def oracle_quant(scheme, x):
+    if scheme == W8A8:
+        return O.quant_act_int8(x)
+    return O.quant_act_fp8(x, 128 if scheme == FP8B else 0)
+
+
+def exact(scheme, qx, sx, qw, sw):
+    if scheme == W8A8:
+        return O.rescale_rowwise(O.contract_int8(qx, qw), sx, sw)
+    if scheme == FP8R:
+        return O.rescale_rowwise(O.contract_e4m3(qx, qw), sx, sw)
+    return O.rescale_block(O.contract_e4m3_blocks(qx, qw), sx, sw)
+
+
+CASES = [
+    # (M, K, segment widths)
+    (1, 128, [128]),
+    (1, 4096, [4096, 1024, 1024]),          # q, k, v of one layer
+    (1, 4096, [14336, 14336]),              # gate, up
+    (1, 14336, [4096]),                     # down
+    (1, 12288, [4096]),                     # Qwen3 down
+    (1, 1152, [256, 384, 128, 640]),        # four segments, ragged widths
+    (3, 1024, [256, 128]),                  # staged path (small M)
+    (40, 512, [384]),                       # staged path (tiled GEMM)
+]
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R, FP8B])
+@pytest.mark.parametrize("M,K,ns", CASES)
+def test_linear_matches_oracle(scheme, M, K, ns):
+    x = W.x_bf16(7000 + M + K + len(ns), M, K)
+    segs = make_segments(scheme, 7100 + K, ns, K)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
+    for staged in ((False, True) if M == 1 else (True,)):
+        ys, qx, sx = run_linear(scheme, x, segs, BF16, staged)
+        if qx is not None:
+            if scheme == W8A8:
+                assert np.array_equal(qx.view(np.int8), qx_ref)
+            else:
+                assert e4m3_equal_mod_zero(qx, qx_ref)
+            assert np.array_equal(sx.view(np.uint32), sx_ref.view(np.uint32))
+        for (qw, sw), y in zip(segs, ys):
+            ye = exact(scheme, qx_ref, sx_ref, qw, sw)
+            assert_within_tol(y, ye, f"scheme {scheme} staged {staged}")
+            if scheme == W8A8:
+                acc = O.contract_int8(qx_ref, qw)
+                assert np.array_equal(y, O.epilogue_f32_order(acc, sx_ref, sw))
+
+
+def test_linear_int8_accumulator_exact():
+    x = W.x_bf16(7300, 1, 4096)
+    segs = make_segments(W8A8, 7301, [4096, 1024, 1024], 4096)
+    qx_ref, _ = O.quant_act_int8(x)
+    ys, _, _ = run_linear(W8A8, x, segs, I32, False)
+    for (qw, _), y in zip(segs, ys):
+        assert np.array_equal(y, O.contract_int8(qx_ref, qw))
+
+
+def test_linear_zero_row_and_empty_segment():
+    torch = torch_mod()
+    x = np.zeros((1, 256), np.uint16)
+    qw = W.w_int8(7400, 64, 256)
+    sw = W.scale_bf16(7401, 64)
+    y = empty(torch, (1, 64), torch.int16, fill=0x7F)
+    empty_w = torch.empty((0, 256), dtype=torch.int8, device="cuda")
+    Q().qlin_linear(W8A8, dev(x), [(dev(qw), dev(sw), y), (empty_w, None, None)])
+    assert not host(y).any()                 # all-zero token -> s = 0 -> y = 0
+
+
+def test_linear_long_k_uses_staging():
+    # K above the one-launch limit at M = 1: q_x / s_x are required staging
+    torch = torch_mod()
+    K = 16400
+    x = W.x_bf16(7500, 1, K)
+    qw = W.w_int8(7501, 40, K)
+    sw = W.scale_bf16(7502, 40)
+    y = empty(torch, (1, 40), torch.int16)
+    with pytest.raises(Q().QlinError):
+        Q().qlin_linear(W8A8, dev(x), [(dev(qw), dev(sw), y)])
+    ys, qx, sx = run_linear(W8A8, x, [(qw, sw)], BF16, True)
+    qx_ref, sx_ref = O.quant_act_int8(x)
+    assert np.array_equal(qx.view(np.int8), qx_ref)
+    assert np.array_equal(ys[0], O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
