@@ -80,7 +80,12 @@ typedef enum qlin_path {
     QLIN_PATH_AUTO = 0,
     QLIN_PATH_GEMV = 1,   /* M must be 1 */
     QLIN_PATH_SMALL = 2,  /* M must be <= 32 */
-    QLIN_PATH_LARGE = 3   /* any M */
+    QLIN_PATH_LARGE = 3,  /* any M; tile shape chosen from M and N */
+    /* the tiled GEMM with one fixed output tile (weight rows x tokens), any M */
+    QLIN_PATH_LARGE_256X128 = 4,
+    QLIN_PATH_LARGE_128X128 = 5,
+    QLIN_PATH_LARGE_128X64 = 6,
+    QLIN_PATH_LARGE_128X256 = 7
 } qlin_path;
 
 /* ---------------------------------------------------------------------- */

@@ -19,6 +19,8 @@ OUT_BF16, OUT_I32, OUT_F32 = 0, 1, 2
 SCHEME_W8A8, SCHEME_FP8_ROWWISE, SCHEME_FP8_BLOCK = 0, 1, 2
 MAX_SEGMENTS = 4
 PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_LARGE = 0, 1, 2, 3
+# the tiled GEMM with a fixed output tile (weight rows x tokens)
+PATH_LARGE_256X128, PATH_LARGE_128X128, PATH_LARGE_128X64, PATH_LARGE_128X256 = 4, 5, 6, 7
 ABI_VERSION = 1
 MAX_K = 131072
 

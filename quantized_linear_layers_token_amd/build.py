@@ -1,6 +1,7 @@
 """Build libqlin.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-Usage: python -m quantized_linear_layers_token_amd.build
+Usage: python quantized_linear_layers_token_amd/build.py   (by path: importing the
+package itself loads the library)
 """
 from __future__ import annotations
 

@@ -2,26 +2,34 @@
 // inputs rounded a row at a time and multiplied in int8, summing in int32;
 // Qwen3 8B FP8 card, "Loading": block-scaled FP8 product).
 //
-// Tiled GEMM, both operands K-contiguous ("NT"): the output tile is BN
-// weight rows x BM tokens; 256 threads = 4 wavefronts in a 2 x 2 grid, each
-// owning a (BN/2) x (BM/2) sub-tile made of 32 x 32 MFMA tiles:
-//   int8: v_mfma_i32_32x32x32_i8  (4 per 128-byte K stage)
-//   E4M3: v_mfma_f32_32x32x64_f8f6f4 (2 per 128-byte K stage)
-// K advances in stages of 128 bytes through a double-buffered LDS tile: the
-// next stage's global loads are in flight while the current stage is
-// multiplied, then land in the other buffer; one barrier per stage.  LDS rows
-// are 128 bytes with the 16-byte chunk index XOR-swizzled by (row & 7) so that
-// the MFMA operand reads (eight rows, same chunk) hit distinct banks.
+// Tiled GEMM, both operands K-contiguous.  Output tile = BN weight rows x BM
+// tokens, 256 threads = 4 wavefronts in a WN x WM grid; a wave owns a
+// (BN/WN) x (BM/WM) sub-tile of 32 x 32 MFMA tiles:
+//   int8: v_mfma_i32_32x32x32_i8      (4 per 128-byte K stage)
+//   E4M3: v_mfma_f32_32x32x64_f8f6f4  (2 per 128-byte K stage)
+// (the 16x16 int8 MFMA runs at about half the 32x32 rate on gfx950, and large
+// wave tiles keep the LDS operand reads under the ~128 B/clk LDS port).
+//
+// K advances in 128-byte stages.  Pipeline: stage s is loaded from global
+// memory into one of two register sets at iteration s - 2, written to one of
+// two LDS buffers at iteration s - 1, and multiplied at iteration s; one
+// barrier per stage.  Register loads give the compiler exact per-register wait
+// counts, so two stages of loads stay in flight while a stage is multiplied.
+// (Direct global->LDS loads were tried: the compiler then drains every load in
+// flight before any LDS read of the tile.)  LDS rows are 128 bytes with the
+// 16-byte chunk index XOR-swizzled by (row & 7), so the MFMA operand reads
+// (eight rows, one logical chunk) hit eight distinct bank groups.
 //
 // A operand = weight rows (n), B operand = tokens (m): a lane's 16 accumulator
-// values are 16 rows n of one token column m, all inside one 32-row slab.  For
-// block FP8 each stage is exactly one 128-wide K block, so one factor
-// s_x[m, kb] * s_w[n/128, kb] per lane and MFMA tile scales the stage's partial
-// product before it is added to the f32 accumulator.
+// values are 16 rows n of one token column m inside one 32-row slab.  For block
+// FP8 a stage is exactly one 128-wide K block: the stage's partial product is
+// scaled by s_x[m, kb] * s_w[n/128, kb] (one factor per lane and MFMA tile)
+// and added to the f32 accumulator; the factors ride with the stage's loads.
 //
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8; tile ids are
-// assigned so that the tiles sharing one weight panel (same n tile) are
-// consecutive on one XCD and share its L2.
+// assigned so that tiles sharing a weight panel are consecutive on one XCD.
+#include <type_traits>
+
 #include "qlin_device.h"
 #include "qlin_internal.h"
 
@@ -29,76 +37,124 @@ namespace qlin {
 
 namespace {
 
-constexpr int kLargeThreads = 256;
+constexpr int kThreads = 256;
 constexpr int kBK = 128;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor, 32-bit data format (gfx9 family)
 
 template <int V> struct LargeAcc { typedef v16i T; };
 template <> struct LargeAcc<VAR_FP8_ROW> { typedef v16f T; };
 template <> struct LargeAcc<VAR_FP8_BLOCK> { typedef v16f T; };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+template <int U> using IC = std::integral_constant<int, U>;
 
-template <int V, int BN, int BM>
-__global__ __launch_bounds__(kLargeThreads) void gemm_large_kernel(
+template <int V, int BN, int BM, int WN, int WM>
+__global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ sw,
     void* __restrict__ y, int M, int N, int K, int mode, int tiles_m, int tiles_n) {
     typedef typename LargeAcc<V>::T Acc;
-    constexpr int WN = BN / 2, WM = BM / 2;
-    constexpr int TN = WN / 32, TM = WM / 32;
-    constexpr int CA = BN * 8 / kLargeThreads;   // 16-byte chunks per thread per stage (weights)
-    constexpr int CB = BM * 8 / kLargeThreads;   // (tokens)
-    static_assert(CA >= 1 && CB >= 1, "tile too small for 256 threads");
-    constexpr int TILE_BYTES = (BN + BM) * kBK;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TILE_BYTES];
+    static_assert(WN * WM == 4, "four wavefronts");
+    constexpr int SN = BN / WN, SM = BM / WM;              // wave sub-tile
+    constexpr int TN = SN / 32, TM = SM / 32;              // 32x32 MFMA tiles per wave
+    constexpr int ROWS = BN + BM;                          // LDS rows per stage (weights first)
+    constexpr int STAGE = ROWS * kBK;
+    constexpr int CH = ROWS * 8 / kThreads;                // 16-byte chunks per thread per stage
+    static_assert(ROWS * 8 % kThreads == 0 && TN >= 1 && TM >= 1 && SN % 32 == 0 && SM % 32 == 0, "tile");
+    // MFMA groups per stage at which loads are issued (see compute)
+    constexpr int HOOKS = V == VAR_INT8 ? 4 * TN : (V == VAR_FP8_ROW ? 2 * TN : TN * TM);
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+    __shared__ float s_w_t[BN], s_x_t[BM];                // rowwise schemes: this tile's scales
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wn = wave >> 1, wm = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave / WM, wm = wave % WM;
 
-    // XCD-aware tile order (identity when the tile count is not a multiple of 8).
     const int ntiles = tiles_m * tiles_n;
     const int b = blockIdx.x;
     const int t = (ntiles & 7) ? b : ((b & 7) * (ntiles >> 3) + (b >> 3));
     const int n0 = (t / tiles_m) * BN;
     const int m0 = (t % tiles_m) * BM;
 
-    // Global -> register staging assignment: chunk i = tid + 256 j -> (row i/8, chunk i%8).
-    const uint8_t* ga[CA];
-    const uint8_t* gb[CB];
-    int la[CA], lb[CB];
+    // ---- global -> register -> LDS assignment.  Thread tid carries logical
+    // 16-byte chunk tid % 8 of rows tid / 8 + 32 j.  Loads go through buffer
+    // descriptors spanning this tile's weight rows and token rows: rows past N
+    // or M lie outside the descriptor's range and read as zero.
+    constexpr int JW = BN / 32, JX = BM / 32, JR = JW > JX ? JW : JX;
+    static_assert(JW + JX == CH, "chunk split");
+    const int cthr = tid & 7;
+    const __amdgpu_buffer_rsrc_t dw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qw + (int64_t)n0 * K), 0, min(BN, N - n0) * K, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qx + (int64_t)m0 * K), 0, min(BM, M - m0) * K, kRsrcWord3);
+    int roff[JR];                                          // byte offset of each carried row
 #pragma unroll
-    for (int j = 0; j < CA; ++j) {
-        const int i = tid + j * kLargeThreads, row = i >> 3, c = i & 7;
-        ga[j] = qw + (int64_t)min(n0 + row, N - 1) * K + c * 16;
-        la[j] = swz(row, c);
-    }
-#pragma unroll
-    for (int j = 0; j < CB; ++j) {
-        const int i = tid + j * kLargeThreads, row = i >> 3, c = i & 7;
-        gb[j] = qx + (int64_t)min(m0 + row, M - 1) * K + c * 16;
-        lb[j] = BN * kBK + swz(row, c);
-    }
-    const int cthr = (tid & 7) * 16;   // this thread's chunk offset inside a stage (same for all j)
+    for (int j = 0; j < JR; ++j) roff[j] = ((tid >> 3) + 32 * j) * K;
+    // LDS byte offset of carried row j: row r = tid / 8 + 32 j keeps r & 7
+    const int loff0 = (tid >> 3) * kBK + ((cthr ^ ((tid >> 3) & 7)) << 4);
+    const int nk = (K + kBK - 1) / kBK;
+    const int kbs = K >> 7;
 
-    v4u ra[CA], rb[CB];
-    auto load_stage = [&](int kt) {
-        const int k = kt * kBK + cthr;
-        const bool ok = k < K;
-#pragma unroll
-        for (int j = 0; j < CA; ++j)
-            ra[j] = ok ? *reinterpret_cast<const v4u*>(ga[j] + (int64_t)kt * kBK) : v4u{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < CB; ++j)
-            rb[j] = ok ? *reinterpret_cast<const v4u*>(gb[j] + (int64_t)kt * kBK) : v4u{0, 0, 0, 0};
+    // Register staging: stage s is loaded into register set s % 2 while stage
+    // s - 2 is multiplied, and written to LDS buffer s % 2 after stage s - 1
+    // is multiplied.  The loads are spread between the MFMAs (hook points in
+    // compute) so that the address unit is never handed a burst that stalls
+    // MFMA issue.  Block FP8: a stage's factors load with the set and move to
+    // the buffer's copy when the set is written.
+    v4u rx[CH], ry[CH];
+    float fxx[TM], fwx[TN], fxy[TM], fwy[TN];             // factors of the register sets
+    float fx0[TM], fw0[TN], fx1[TM], fw1[TN];             // factors of the LDS buffers
+    auto issue_one = [&](auto set, int s, int j) {
+        v4u(&r)[CH] = decltype(set)::value ? ry : rx;
+        // chunks past K re-read the row's last chunk (zeroed when written to LDS),
+        // so every in-range offset stays inside its row
+        const int k = min(s * kBK + cthr * 16, K - 16);
+        if (j < JW) r[j] = __builtin_amdgcn_raw_buffer_load_b128(dw, roff[j] + k, 0, 0);
+        else r[j] = __builtin_amdgcn_raw_buffer_load_b128(dx, roff[j - JW] + k, 0, 0);
     };
-    auto store_stage = [&](int buf) {
-        uint8_t* base = lds + buf * TILE_BYTES;
+    auto issue_fac = [&](auto set, int s) {
+        if constexpr (V == VAR_FP8_BLOCK) {
+            float(&fx)[TM] = decltype(set)::value ? fxy : fxx;
+            float(&fw)[TN] = decltype(set)::value ? fwy : fwx;
+            const int kb = min(s, kbs - 1);                    // a stage past the end reloads the last block's factors
 #pragma unroll
-        for (int j = 0; j < CA; ++j) *reinterpret_cast<v4u*>(base + la[j]) = ra[j];
+            for (int jj = 0; jj < TM; ++jj)
+                fx[jj] = sx[(int64_t)min(m0 + wm * SM + jj * 32 + (lane & 31), M - 1) * kbs + kb];
 #pragma unroll
-        for (int j = 0; j < CB; ++j) *reinterpret_cast<v4u*>(base + lb[j]) = rb[j];
+            for (int ii = 0; ii < TN; ++ii)
+                fw[ii] = bf16_lo(sw[(int64_t)(min(n0 + wn * SN + ii * 32, N - 1) >> 7) * kbs + kb]);
+        }
+    };
+    auto issue_all = [&](auto set, int s) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) issue_one(set, s, j);
+        issue_fac(set, s);
+    };
+    // hook point h of HOOKS in one stage's MFMA sequence: its share of the loads
+    auto hook = [&](auto set, int s, int h) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (h == 0) issue_fac(set, s);
+#pragma unroll
+        for (int j = h * CH / HOOKS; j < (h + 1) * CH / HOOKS; ++j) issue_one(set, s, j);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto write = [&](auto set, auto buf, int s) {
+        const v4u(&r)[CH] = decltype(set)::value ? ry : rx;
+        uint8_t* base = lds + decltype(buf)::value * STAGE;
+        const bool ok = s * kBK + cthr * 16 < K;           // false in a ragged last stage and past the end
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = ok ? r[j] : v4u{0, 0, 0, 0};
+        if constexpr (V == VAR_FP8_BLOCK) {
+            const float(&fxs)[TM] = decltype(set)::value ? fxy : fxx;
+            const float(&fws)[TN] = decltype(set)::value ? fwy : fwx;
+            float(&fxb)[TM] = decltype(buf)::value ? fx1 : fx0;
+            float(&fwb)[TN] = decltype(buf)::value ? fw1 : fw0;
+#pragma unroll
+            for (int jj = 0; jj < TM; ++jj) fxb[jj] = fxs[jj];
+#pragma unroll
+            for (int ii = 0; ii < TN; ++ii) fwb[ii] = fws[ii];
+        }
     };
 
     Acc acc[TN][TM];
@@ -107,138 +163,239 @@ __global__ __launch_bounds__(kLargeThreads) void gemm_large_kernel(
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = Acc{};
 
-    // Operand rows inside the LDS tile for this lane.
-    const int arow0 = wn * WN + (lane & 31);
-    const int brow0 = BN + wm * WM + (lane & 31);   // B rows follow the BN weight rows
+    const int arow0 = wn * SN + (lane & 31);
+    const int brow0 = BN + wm * SM + (lane & 31);
     const int half = lane >> 5;
 
-    const int nk = (K + kBK - 1) / kBK;
-    const int kbs = K >> 7;
+    if constexpr (V != VAR_FP8_BLOCK) {
+        // the epilogue's scales, staged once
+        for (int i = tid; i < BN; i += kThreads) s_w_t[i] = bf16_lo(sw[min(n0 + i, N - 1)]);
+        for (int i = tid; i < BM; i += kThreads) s_x_t[i] = sx[min(m0 + i, M - 1)];
+    }
 
-    load_stage(0);
-    store_stage(0);
+    // prologue: stage 0 in LDS buffer 0, stage 1 in flight
+    issue_all(IC<0>{}, 0);
+    write(IC<0>{}, IC<0>{}, 0);
+    issue_all(IC<1>{}, 1);
     __syncthreads();
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_stage(kt + 1);
-        const uint8_t* base = lds + buf * TILE_BYTES;
-
-        float fx[TM], fw[TN];
-        if constexpr (V == VAR_FP8_BLOCK) {
-#pragma unroll
-            for (int j = 0; j < TM; ++j)
-                fx[j] = sx[(int64_t)min(m0 + wm * WM + j * 32 + (lane & 31), M - 1) * kbs + kt];
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-                fw[i] = bf16_lo(sw[(int64_t)(min(n0 + wn * WN + i * 32, N - 1) >> 7) * kbs + kt]);
-        }
-
+    auto compute = [&](auto buf, const float (&fx)[TM], const float (&fw)[TN], auto&& hk) {
+        const uint8_t* base = lds + decltype(buf)::value * STAGE;
         if constexpr (V == VAR_INT8) {
+            constexpr int SUB = 4;                    // 32-byte K sub-steps per stage
+            v4i a[SUB][TN], bb[SUB][TM];
+            auto rd = [&](int sub) {
+                const int c = 2 * sub + half;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int c = 2 * s + half;
-                v4i a[TN], bb[TM];
+                for (int i = 0; i < TN; ++i) {
+                    const int r = arow0 + i * 32;
+                    a[sub][i] = *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ (r & 7)) << 4));
+                }
 #pragma unroll
-                for (int i = 0; i < TN; ++i)
-                    a[i] = *reinterpret_cast<const v4i*>(base + ((arow0 + i * 32) * kBK + ((c ^ ((arow0 + i * 32) & 7)) << 4)));
+                for (int j = 0; j < TM; ++j) {
+                    const int r = brow0 + j * 32;
+                    bb[sub][j] = *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ (r & 7)) << 4));
+                }
+            };
+            auto mm = [&](int sub) {
 #pragma unroll
-                for (int j = 0; j < TM; ++j)
-                    bb[j] = *reinterpret_cast<const v4i*>(base + ((brow0 + j * 32) * kBK + ((c ^ ((brow0 + j * 32) & 7)) << 4)));
-#pragma unroll
-                for (int i = 0; i < TN; ++i)
+                for (int i = 0; i < TN; ++i) {
 #pragma unroll
                     for (int j = 0; j < TM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
-            }
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[sub][i], bb[sub][j], acc[i][j], 0, 0, 0);
+                    hk(sub * TN + i);
+                }
+            };
+            // the reads of sub-step s + 1 are in flight while the MFMAs of s run
+            rd(0);
+            rd(1);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(0);
+            __builtin_amdgcn_sched_barrier(0);
+            rd(2);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(1);
+            __builtin_amdgcn_sched_barrier(0);
+            rd(3);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(2);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(3);
         } else {
-            v16f part[TN][TM];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int c0 = 4 * s + 2 * half;
-                v8i a[TN], bb[TM];
+            v8i a[2][TN], bb[2][TM];
+            auto rd = [&](int sub) {
+                const int c0 = 4 * sub + 2 * half;
 #pragma unroll
                 for (int i = 0; i < TN; ++i) {
                     const int r = arow0 + i * 32;
                     const v4i lo = *reinterpret_cast<const v4i*>(base + r * kBK + ((c0 ^ (r & 7)) << 4));
                     const v4i hi = *reinterpret_cast<const v4i*>(base + r * kBK + (((c0 + 1) ^ (r & 7)) << 4));
-                    a[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    a[sub][i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 }
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
                     const int r = brow0 + j * 32;
                     const v4i lo = *reinterpret_cast<const v4i*>(base + r * kBK + ((c0 ^ (r & 7)) << 4));
                     const v4i hi = *reinterpret_cast<const v4i*>(base + r * kBK + (((c0 + 1) ^ (r & 7)) << 4));
-                    bb[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    bb[sub][j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 }
+            };
+            rd(0);
+            __builtin_amdgcn_sched_barrier(0);
+            rd(1);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (V == VAR_FP8_ROW) {
 #pragma unroll
-                for (int i = 0; i < TN; ++i)
+                for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int j = 0; j < TM; ++j) {
-                        if constexpr (V == VAR_FP8_ROW) {
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-                        } else {
-                            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                a[i], bb[j], s == 0 ? v16f{} : part[i][j], 0, 0, 0, 0, 0, 0);
-                        }
+                    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+                        for (int j = 0; j < TM; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[sub][i], bb[sub][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                        hk(sub * TN + i);
                     }
-            }
-            if constexpr (V == VAR_FP8_BLOCK) {
+            } else {
+                // one MFMA tile at a time: the block's partial product of tile t is
+                // scaled into the accumulator while the MFMAs of tile t + 1 run,
+                // so only two partial tiles are live
+                constexpr int NT = TN * TM;
+                v16f part[2];
 #pragma unroll
-                for (int i = 0; i < TN; ++i)
-#pragma unroll
-                    for (int j = 0; j < TM; ++j) {
+                for (int t = 0; t <= NT; ++t) {
+                    if (t < NT) {
+                        const int i = t / TM, j = t % TM;
+                        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][i], bb[0][j], v16f{}, 0, 0, 0, 0, 0, 0);
+                        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][i], bb[1][j], part[t & 1], 0, 0, 0, 0, 0, 0);
+                    }
+                    if (t > 0) {
+                        const int i = (t - 1) / TM, j = (t - 1) % TM;
                         const float f = fx[j] * fw[i];
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(part[i][j][e], f, acc[i][j][e]);
+                        for (int e = 0; e < 16; ++e)
+                            acc[i][j][e] = __builtin_fmaf(part[(t - 1) & 1][e], f, acc[i][j][e]);
                     }
+                    if (t < NT) hk(t);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
+    };
 
-        if (kt + 1 < nk) store_stage(buf ^ 1);
+    // Step kt multiplies LDS buffer kt % 2 while the loads of a later stage
+    // run between its MFMAs, writes the next stage into the other buffer and
+    // meets the barrier.  Unrolled by two so that buffers and register sets
+    // are compile-time choices; a single loop exit keeps the accumulators in
+    // place (an odd last stage runs after the loop).  Loads and writes run
+    // unconditionally: a stage past the end re-reads in-range bytes and
+    // writes zeros to a buffer that is not multiplied again (a conditional
+    // load makes the compiler assume the shallower pipeline everywhere).
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        compute(IC<0>{}, fx0, fw0, [&](int h) { hook(IC<0>{}, kt + 2, h); });
+        write(IC<1>{}, IC<1>{}, kt + 1);
+        __syncthreads();
+        compute(IC<1>{}, fx1, fw1, [&](int h) { hook(IC<1>{}, kt + 3, h); });
+        write(IC<0>{}, IC<0>{}, kt + 2);
         __syncthreads();
     }
+    if (kt < nk) compute(IC<0>{}, fx0, fw0, [&](int) {});
 
     // Epilogue.  Lane l, accumulator element e of MFMA tile (i, j):
-    //   n = n0 + wn*WN + i*32 + 8*(e/4) + 4*(l/32) + e%4,   m = m0 + wm*WM + j*32 + l%32.
+    //   n = n0 + wn*SN + i*32 + 8*(e/4) + 4*(l/32) + e%4,   m = m0 + wm*SM + j*32 + l%32,
+    // so elements 4g .. 4g+3 are four consecutive outputs of one row: one 8-byte
+    // (bf16) or 16-byte (f32 / i32) store when the row length allows it.
+    const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-        const int m = m0 + wm * WM + j * 32 + (lane & 31);
+        const int ml = wm * SM + j * 32 + (lane & 31);
+        const int m = m0 + ml;
         if (m >= M) continue;
-        const float sxm = (V == VAR_FP8_BLOCK) ? 0.0f : sx[m];
+        const float sxm = (V == VAR_FP8_BLOCK) ? 0.0f : s_x_t[ml];
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int n = n0 + wn * WN + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-                if (n >= N) continue;
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * SN + i * 32 + 8 * g + 4 * half;
+                const int n = n0 + nl;
                 const int64_t idx = (int64_t)m * N + n;
-                if constexpr (V == VAR_INT8) store_rowwise_i32acc(y, idx, acc[i][j][e], sxm, sw[n], mode);
-                else if constexpr (V == VAR_FP8_ROW) store_f32(y, idx, acc[i][j][e] * (sxm * bf16_lo(sw[n])), mode);
-                else store_f32(y, idx, acc[i][j][e], mode);
+                if (vec && n + 3 < N) {
+                    if constexpr (V == VAR_INT8) {
+                        const int a[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                        const float w4[4] = {s_w_t[nl], s_w_t[nl + 1], s_w_t[nl + 2], s_w_t[nl + 3]};
+                        store4_rowwise_i32acc(y, idx, a, sxm, w4, mode);
+                    } else if constexpr (V == VAR_FP8_ROW) {
+                        const float v4[4] = {acc[i][j][4 * g] * (sxm * s_w_t[nl]), acc[i][j][4 * g + 1] * (sxm * s_w_t[nl + 1]),
+                                             acc[i][j][4 * g + 2] * (sxm * s_w_t[nl + 2]), acc[i][j][4 * g + 3] * (sxm * s_w_t[nl + 3])};
+                        store4_f32(y, idx, v4, mode);
+                    } else {
+                        const float v4[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                        store4_f32(y, idx, v4, mode);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (n + k >= N) break;
+                        const int e = 4 * g + k;
+                        if constexpr (V == VAR_INT8) store_rowwise_i32acc(y, idx + k, acc[i][j][e], sxm, sw[n + k], mode);
+                        else if constexpr (V == VAR_FP8_ROW) store_f32(y, idx + k, acc[i][j][e] * (sxm * s_w_t[nl + k]), mode);
+                        else store_f32(y, idx + k, acc[i][j][e], mode);
+                    }
+                }
             }
         }
     }
 }
 
-template <int V, int BN, int BM>
+template <int V, int BN, int BM, int WN, int WM>
 hipError_t launch_tile(const uint8_t* qx, const float* sx, const uint8_t* qw, const uint16_t* sw, void* y,
                        int64_t M, int64_t N, int64_t K, int mode, hipStream_t st) {
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-    dim3 grid((unsigned)(tm * tn)), block(kLargeThreads);
-    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM>), grid, block, 0, st, qx, sx, qw, sw, y, (int)M, (int)N,
-                       (int)K, mode, tm, tn);
+    dim3 grid((unsigned)(tm * tn)), block(kThreads);
+    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM>), grid, block, 0, st, qx, sx, qw, sw, y,
+                       (int)M, (int)N, (int)K, mode, tm, tn);
     return hipGetLastError();
+}
+
+template <int V>
+hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const uint8_t* qw, const uint16_t* sw,
+                          void* y, int64_t M, int64_t N, int64_t K, int mode, hipStream_t st) {
+    switch (cfg) {
+        case kTile256x128: return launch_tile<V, 256, 128, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
+        case kTile128x128: return launch_tile<V, 128, 128, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
+        case kTile128x64: return launch_tile<V, 128, 64, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
+        case kTile128x256: return launch_tile<V, 128, 256, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
+// Tile choice (measured on the Llama-8B projections at 512 and 1024 tokens):
+// 128 x 128 once it yields three quarters of a workgroup per CU, else
+// 128 x 64 to keep every CU busy.  The 256-row tiles need more load bandwidth
+// per CU than the 64-byte-per-clock vector memory path sustains next to the
+// LDS traffic, and lose on every shape measured.
+int large_tile_config(int64_t M, int64_t N) {
+    const int64_t cus = 256;
+    if (((M + 127) / 128) * ((N + 127) / 128) >= cus * 3 / 4) return kTile128x128;
+    return kTile128x64;
+}
+
+hipError_t launch_gemm_large_cfg(int cfg, int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
+                                 const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
+                                 hipStream_t st) {
+    if (variant == VAR_INT8) return launch_variant<VAR_INT8>(cfg, qx, sx, qw, sw, y, M, N, K, mode, st);
+    if (variant == VAR_FP8_ROW) return launch_variant<VAR_FP8_ROW>(cfg, qx, sx, qw, sw, y, M, N, K, mode, st);
+    return launch_variant<VAR_FP8_BLOCK>(cfg, qx, sx, qw, sw, y, M, N, K, mode, st);
+}
+
 hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
                              const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
                              hipStream_t st) {
-    if (variant == VAR_INT8) return launch_tile<VAR_INT8, 128, 128>(qx, sx, qw, sw, y, M, N, K, mode, st);
-    if (variant == VAR_FP8_ROW) return launch_tile<VAR_FP8_ROW, 128, 128>(qx, sx, qw, sw, y, M, N, K, mode, st);
-    return launch_tile<VAR_FP8_BLOCK, 128, 128>(qx, sx, qw, sw, y, M, N, K, mode, st);
+    // block FP8 scales every stage's partial products on the vector ALUs; the
+    // smaller wave tile keeps those registers in budget and measured fastest
+    const int cfg = variant == VAR_FP8_BLOCK ? kTile128x64 : large_tile_config(M, N);
+    return launch_gemm_large_cfg(cfg, variant, qx, sx, qw, sw, y, M, N, K, mode, st);
 }
 
 }  // namespace qlin

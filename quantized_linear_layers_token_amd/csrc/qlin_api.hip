@@ -42,8 +42,7 @@ qlin_status check_product(int variant, const void* q_x, const float* s_x, const 
     if (variant == qlin::VAR_FP8_BLOCK && ((N % 128) != 0 || (K % 128) != 0)) return QLIN_ERR_SHAPE;
     if (out != QLIN_OUT_BF16 && out != QLIN_OUT_F32 && out != QLIN_OUT_I32) return QLIN_ERR_UNSUPPORTED;
     if (out == QLIN_OUT_I32 && variant != qlin::VAR_INT8) return QLIN_ERR_UNSUPPORTED;
-    if (path != QLIN_PATH_AUTO && path != QLIN_PATH_GEMV && path != QLIN_PATH_SMALL && path != QLIN_PATH_LARGE)
-        return QLIN_ERR_UNSUPPORTED;
+    if (path < QLIN_PATH_AUTO || path > QLIN_PATH_LARGE_128X256) return QLIN_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) {
         *noop = true;
         return QLIN_OK;
@@ -76,7 +75,9 @@ qlin_status run_product(int variant, const void* q_x, const float* s_x, const vo
     hipError_t e;
     if (p == QLIN_PATH_GEMV) e = qlin::launch_gemv(variant, qx, s_x, qw, s_w, y, N, K, (int)out, stream);
     else if (p == QLIN_PATH_SMALL) e = qlin::launch_gemm_small(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
-    else e = qlin::launch_gemm_large(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
+    else if (p == QLIN_PATH_LARGE) e = qlin::launch_gemm_large(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
+    else e = qlin::launch_gemm_large_cfg((int)p - (int)QLIN_PATH_LARGE_256X128, variant, qx, s_x, qw, s_w, y, M, N, K,
+                                         (int)out, stream);
     return hip_status(e);
 }
 

@@ -129,6 +129,37 @@ __device__ __forceinline__ void store_f32(void* y, int64_t idx, float v, int mod
     else static_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
 }
 
+// Four consecutive outputs y[idx .. idx+3] of one row (idx % 4 == 0 and the row
+// length a multiple of 4, so the store is 8- or 16-byte aligned).  Same
+// arithmetic as the scalar stores above: fl32(acc) * fl32(s_x * s_w), RNE.
+__device__ __forceinline__ void store4_rowwise_i32acc(void* y, int64_t idx, const int (&acc)[4], float sx,
+                                                      const float (&sw)[4], int mode) {
+    if (mode == OUT_I32) {
+        *reinterpret_cast<v4i*>(static_cast<int*>(y) + idx) = v4i{acc[0], acc[1], acc[2], acc[3]};
+        return;
+    }
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (float)acc[k] * (sx * sw[k]);
+    if (mode == OUT_F32) {
+        *reinterpret_cast<v4f*>(static_cast<float*>(y) + idx) = v4f{v[0], v[1], v[2], v[3]};
+    } else {
+        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<v2u*>(static_cast<uint16_t*>(y) + idx) = v2u{lo, hi};
+    }
+}
+
+__device__ __forceinline__ void store4_f32(void* y, int64_t idx, const float (&v)[4], int mode) {
+    if (mode == OUT_F32) {
+        *reinterpret_cast<v4f*>(static_cast<float*>(y) + idx) = v4f{v[0], v[1], v[2], v[3]};
+    } else {
+        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<v2u*>(static_cast<uint16_t*>(y) + idx) = v2u{lo, hi};
+    }
+}
+
 // E4M3 pair decode (bytes 0/1 when HI == false, bytes 2/3 when HI == true).
 typedef float v2f __attribute__((ext_vector_type(2)));
 template <bool HI>

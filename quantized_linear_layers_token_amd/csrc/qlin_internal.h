@@ -29,6 +29,13 @@ hipError_t launch_gemv(int variant, const uint8_t* qx, const float* sx, const ui
 hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
                              const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
                              hipStream_t st);
+// Output tiles of the tiled GEMM (weight rows x tokens), in the order of the
+// fixed-tile paths of the C ABI.
+enum LargeTile : int { kTile256x128 = 0, kTile128x128 = 1, kTile128x64 = 2, kTile128x256 = 3 };
+hipError_t launch_gemm_large_cfg(int cfg, int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
+                                 const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
+                                 hipStream_t st);
+int large_tile_config(int64_t M, int64_t N);
 hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
                              const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
                              hipStream_t st);

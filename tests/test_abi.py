@@ -94,7 +94,8 @@ def test_product_validation(fn):
     assert gemm(fn, *args[:4], b["y"] + 2, 4, 256, 256) == Q.QLIN_ERR_ALIGN
     assert gemm(fn, *args[:3], b["sw"] + 1, b["y"], 4, 256, 256) == Q.QLIN_ERR_ALIGN
     assert gemm(fn, *args, 4, 256, 256, out=7) == Q.QLIN_ERR_UNSUPPORTED
-    assert gemm(fn, *args, 4, 256, 256, path=9) == Q.QLIN_ERR_UNSUPPORTED
+    assert gemm(fn, *args, 4, 256, 256, path=8) == Q.QLIN_ERR_UNSUPPORTED
+    assert gemm(fn, *args, 4, 256, 256, path=-1) == Q.QLIN_ERR_UNSUPPORTED
     assert gemm(fn, *args, 2, 256, 256, path=Q.PATH_GEMV) == Q.QLIN_ERR_UNSUPPORTED
     assert gemm(fn, *args, 33, 256, 256, path=Q.PATH_SMALL) == Q.QLIN_ERR_UNSUPPORTED
     assert gemm(fn, *args[:4], b["qw"] + 256, 4, 256, 256) == Q.QLIN_ERR_ALIAS    # y overlaps q_w
@@ -161,3 +162,12 @@ def test_linear_validation():
     assert lin(0, x, 1, 256, nul, 1, 0, None, None, None) == Q.QLIN_ERR_NULL
     empty = (Seg * 1)(Seg(None, None, None, 0))
     assert lin(0, x, 1, 256, empty, 1, 0, None, None, None) == Q.QLIN_OK             # no rows: no-op
+
+
+def test_library_has_no_unresolved_internal_symbols():
+    # a kernel whose device code failed to emit leaves its host launch stub
+    # undefined; the loader only notices at the first call
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", Q.LIB_PATH], capture_output=True, text=True).stdout
+    bad = [ln for ln in out.splitlines() if "qlin" in ln]
+    assert not bad, bad

@@ -314,3 +314,42 @@ def test_fp8_mfma_accumulation_model():
     for p in (SMALL, LARGE):
         y = run_product("qlin_gemm_fp8_rowwise", X, sx, Wt, sw, n, n, F32, p)
         assert np.array_equal(np.diag(y).astype(np.float64), exact), p
+
+
+# Every fixed output tile of the tiled GEMM, on shapes spanning several tiles
+# with ragged M, N and K edges, one- to three-stage K (pipeline prologue and the
+# odd last stage) and tile counts that do and do not divide by the 8 XCDs.
+TILE_PATHS = [4, 5, 6, 7]      # 256x128, 128x128, 128x64, 128x256 (weight rows x tokens)
+TILE_SHAPES = [(300, 600, 1040), (129, 257, 16), (40, 130, 384), (512, 1024, 128), (260, 384, 256)]
+TILE_BLOCK_SHAPES = [(300, 640, 1152), (129, 256, 128), (40, 128, 384), (512, 1024, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_int8_every_tile(M, N, K):
+    case = int8_case(11 * M + N + K, M, N, K)
+    for p in TILE_PATHS:
+        check_int8(*case, p)
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_fp8_rowwise_every_tile(M, N, K):
+    qx, sx, qw, sw = fp8_row_case(21 * M + N + K, M, N, K)
+    y_exact = O.rescale_rowwise(O.contract_e4m3(qx, qw), sx, sw)
+    bound = rowwise_bound(qx, qw, sx, sw, LARGE)
+    for p in TILE_PATHS:
+        y = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, N, BF16, p)
+        assert_within_tol(y, y_exact, f"fp8 rowwise tile path {p}")
+        yf = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, N, F32, p)
+        assert np.all(np.abs(yf - y_exact) <= bound), f"f32 result outside the summation bound (path {p})"
+
+
+@pytest.mark.parametrize("M,N,K", TILE_BLOCK_SHAPES)
+def test_fp8_block_every_tile(M, N, K):
+    qx, sx, qw, sw = fp8_block_case(31 * M + N + K, M, N, K)
+    y_exact = O.rescale_block(O.contract_e4m3_blocks(qx, qw), sx, sw)
+    bound = block_bound(qx, qw, sx, sw, LARGE)
+    for p in TILE_PATHS:
+        y = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, N, BF16, p)
+        assert_within_tol(y, y_exact, f"fp8 block tile path {p}")
+        yf = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, N, F32, p)
+        assert np.all(np.abs(yf - y_exact) <= bound), f"f32 result outside the summation bound (path {p})"
