@@ -5,18 +5,22 @@ Headline (`value`): W8A8 decode at one token -- the Llama-3.1-8B projection set
 (per layer q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 14336x4096,
 down 4096x14336), 32 layers with distinct weights (6.98 GB of int8, far above
 the 256 MB Infinity Cache).  One step = one decoded token through all 32
-layers: 4 per-token int8 activation quantizations and 7 one-row products per
-layer (352 kernels), replayed as one HIP graph.  value = algorithmic bytes of
-the step / step time, in GB/s.
+layers: per layer four qlin_linear calls (q/k/v, o, gate/up, down), each one
+launch that rounds the token to int8 and runs the one-row products of every
+projection reading it -- 128 launches, replayed as one HIP graph.
+value = algorithmic bytes of the step / step time, in GB/s.
 
-Also reported (`secondary`): M=512 (and 1024) prefill TOPS for W8A8 int8, FP8
-per-channel (Llama shapes) and FP8 block (Qwen3-8B shapes); per-shape GEMV
-bandwidth; small-M (4..32) fused-projection bandwidth.
+Also reported (`secondary`): the same step as quantize + separate one-row
+products; per-shape one-row bandwidth; small-M (4..32) fused-projection
+bandwidth; M=512 and 1024 prefill TOPS for W8A8 int8, FP8 per-channel (Llama
+shapes) and FP8 block (Qwen3-8B shapes), both as one qlin_linear call per
+input group (quantization + one GEMM launch over q/k/v or gate/up) and as
+separate per-projection GEMMs.
 
-`roofline` is for the dominant kernel, the int8 one-row product: achieved =
-algorithmic bytes per launch / average launch duration measured with HIP events
-around a graph of the 224 products.  `cpu_baseline` times the CPU oracle on a
-bounded sample of the same decode workload.
+`roofline` is for the dominant kernel, the fused one-row decode kernel:
+achieved = algorithmic bytes per launch / average launch duration measured with
+HIP events around a graph of the 128 launches.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same decode workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -198,6 +202,8 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
     shp = dict((n, (N, K)) for n, N, K in shapes)
     full = Launcher(Q, torch)
     prod = Launcher(Q, torch)
+    fused = Launcher(Q, torch)
+    scheme = {"int8": Q.SCHEME_W8A8, "fp8_row": Q.SCHEME_FP8_ROWWISE, "fp8_block": Q.SCHEME_FP8_BLOCK}[variant]
     gen = torch.Generator(device=dev)
     ops = 0
     keep = []
@@ -217,6 +223,7 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
                 s = torch.empty((M, K // 128) if g else (M,), dtype=torch.float32, device=dev)
                 full.quant_fp8(x, q, s, g)
             keep += [x, q, s]
+            segs = []
             for name in group:
                 N, _ = shp[name]
                 if variant == "int8":
@@ -229,8 +236,11 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
                 keep += [qw, sw, y]
                 full.gemm(fn, q, s, qw, sw, y, M, N, K)
                 prod.gemm(fn, q, s, qw, sw, y, M, N, K)
+                segs.append((qw, sw, y))
                 ops += 2 * M * N * K
-    return full, prod, ops, keep
+            # the group as one call: quantization + one GEMM launch over its segments
+            fused.linear(scheme, x, segs, qx=q, sx=s)
+    return full, prod, fused, ops, keep
 
 
 # ---------------------------------------------------------------------------
@@ -401,24 +411,29 @@ def main():
         for variant, peak in (("int8", MFMA_INT8_PEAK_TOPS), ("fp8_row", MFMA_FP8_PEAK_TOPS),
                               ("fp8_block", MFMA_FP8_PEAK_TOPS)):
             for M in (512, 1024):
-                full, prod, ops, keep = prefill_layer_set(torch, Q, W, variant, M, 4, dev,
-                                                          {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
+                full, prod, fused, ops, keep = prefill_layer_set(
+                    torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
                 f_full = capture(torch, full.run, use_graph)
                 f_prod = capture(torch, prod.run, use_graph)
+                f_fused = capture(torch, fused.run, use_graph)
                 f_full()
                 f_prod()
+                f_fused()
                 t_full = time_events(torch, f_full, 5)
                 t_prod = time_events(torch, f_prod, 5)
+                t_fused = time_events(torch, f_fused, 5)
                 key = f"prefill_{variant}_M{M}"
                 secondary[key] = {
-                    "tops_gemm": round(ops / (t_prod * 1e-3) / 1e12, 1),
-                    "frac_gemm": round(ops / (t_prod * 1e-3) / 1e12 / peak, 4),
-                    "tops_with_quant": round(ops / (t_full * 1e-3) / 1e12, 1),
-                    "ms_per_layer_gemm": round(t_prod / 4, 4),
+                    "tops_fused_linear": round(ops / (t_fused * 1e-3) / 1e12, 1),
+                    "frac_fused_linear": round(ops / (t_fused * 1e-3) / 1e12 / peak, 4),
+                    "tops_gemm_per_projection": round(ops / (t_prod * 1e-3) / 1e12, 1),
+                    "frac_gemm_per_projection": round(ops / (t_prod * 1e-3) / 1e12 / peak, 4),
+                    "tops_quant_then_per_projection": round(ops / (t_full * 1e-3) / 1e12, 1),
+                    "ms_per_layer_fused": round(t_fused / 4, 4),
                     "shapes": "qwen3-8b" if variant == "fp8_block" else "llama-3.1-8b",
                 }
                 log(f"{key}: {secondary[key]}")
-                del keep, full, prod, f_full, f_prod
+                del keep, full, prod, fused, f_full, f_prod, f_fused
                 torch.cuda.synchronize()
 
     cpu = None

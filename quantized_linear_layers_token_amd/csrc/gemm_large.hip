@@ -39,7 +39,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor, 32-bit data format (gfx9 family)
 
 template <int V> struct LargeAcc { typedef v16i T; };
 template <> struct LargeAcc<VAR_FP8_ROW> { typedef v16f T; };
@@ -49,9 +48,8 @@ template <int U> using IC = std::integral_constant<int, U>;
 
 template <int V, int BN, int BM, int WN, int WM>
 __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
-    const uint8_t* __restrict__ qx, const float* __restrict__ sx,
-    const uint8_t* __restrict__ qw, const uint16_t* __restrict__ sw,
-    void* __restrict__ y, int M, int N, int K, int mode, int tiles_m, int tiles_n) {
+    const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa,
+    int M, int K, int mode, int tiles_m, int tiles_n) {
     typedef typename LargeAcc<V>::T Acc;
     static_assert(WN * WM == 4, "four wavefronts");
     constexpr int SN = BN / WN, SM = BM / WM;              // wave sub-tile
@@ -73,8 +71,27 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     const int ntiles = tiles_m * tiles_n;
     const int b = blockIdx.x;
     const int t = (ntiles & 7) ? b : ((b & 7) * (ntiles >> 3) + (b >> 3));
-    const int n0 = (t / tiles_m) * BN;
-    const int m0 = (t % tiles_m) * BM;
+    // weight panels are numbered across the segments (q, k, v or gate, up
+    // sharing one input); a panel never straddles two segments.  The integer
+    // division runs on the vector ALU: readfirstlane returns the (uniform)
+    // results to scalar registers, so the buffer descriptors built from them
+    // are scalar (a descriptor the compiler takes as divergent costs a
+    // readfirstlane loop around every load).
+    int panel = __builtin_amdgcn_readfirstlane(t / tiles_m), seg = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < kMaxSegments; ++i) {
+        const int np = (sa.start[i + 1] - sa.start[i] + BN - 1) / BN;
+        if (seg == i && i + 1 < sa.nseg && panel >= np) {
+            panel -= np;
+            seg = i + 1;
+        }
+    }
+    const uint8_t* __restrict__ qw = sa.w[seg];
+    const uint16_t* __restrict__ sw = sa.sw[seg];
+    void* __restrict__ y = sa.y[seg];
+    const int N = sa.start[seg + 1] - sa.start[seg];
+    const int n0 = panel * BN;
+    const int m0 = __builtin_amdgcn_readfirstlane((t % tiles_m) * BM);
 
     // ---- global -> register -> LDS assignment.  Thread tid carries logical
     // 16-byte chunk tid % 8 of rows tid / 8 + 32 j.  Loads go through buffer
@@ -83,10 +100,8 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     constexpr int JW = BN / 32, JX = BM / 32, JR = JW > JX ? JW : JX;
     static_assert(JW + JX == CH, "chunk split");
     const int cthr = tid & 7;
-    const __amdgpu_buffer_rsrc_t dw = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(qw + (int64_t)n0 * K), 0, min(BN, N - n0) * K, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t dx = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(qx + (int64_t)m0 * K), 0, min(BM, M - m0) * K, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(BN, N - n0) * K);
+    const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(qx + (int64_t)m0 * K, min(BM, M - m0) * K);
     int roff[JR];                                          // byte offset of each carried row
 #pragma unroll
     for (int j = 0; j < JR; ++j) roff[j] = ((tid >> 3) + 32 * j) * K;
@@ -302,8 +317,53 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
 
     // Epilogue.  Lane l, accumulator element e of MFMA tile (i, j):
     //   n = n0 + wn*SN + i*32 + 8*(e/4) + 4*(l/32) + e%4,   m = m0 + wm*SM + j*32 + l%32,
-    // so elements 4g .. 4g+3 are four consecutive outputs of one row: one 8-byte
-    // (bf16) or 16-byte (f32 / i32) store when the row length allows it.
+    // so elements 4g .. 4g+3 are four consecutive outputs of one row.
+    //
+    // bf16 output with 16-byte aligned rows goes through LDS: the waves write
+    // their converted sub-tiles into a row-major [BM][BN] tile (row pitch
+    // padded by 16 bytes so the 32 rows of one column group fall on distinct
+    // banks), then every thread streams whole 16-byte pieces of output rows,
+    // a wave covering 1 KB of contiguous rows per store instead of 32 rows x
+    // 16 bytes.
+    if (mode == OUT_BF16 && (N & 7) == 0) {
+        constexpr int PITCH = BN * 2 + 16;
+        static_assert(BM * PITCH <= (int)sizeof(lds), "bf16 staging tile fits the stage buffers");
+        __syncthreads();                                   // every wave is done with the last stage
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int ml = wm * SM + j * 32 + (lane & 31);
+            const float sxm = (V == VAR_FP8_BLOCK) ? 0.0f : s_x_t[ml];
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * SN + i * 32 + 8 * g + 4 * half;
+                    float v[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if constexpr (V == VAR_INT8) v[k] = (float)acc[i][j][4 * g + k] * (sxm * s_w_t[nl + k]);
+                        else if constexpr (V == VAR_FP8_ROW) v[k] = acc[i][j][4 * g + k] * (sxm * s_w_t[nl + k]);
+                        else v[k] = acc[i][j][4 * g + k];
+                    }
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    *reinterpret_cast<v2u*>(lds + ml * PITCH + nl * 2) = v2u{lo, hi};
+                }
+        }
+        __syncthreads();
+        constexpr int CPR = BN * 2 / 16;                   // 16-byte pieces per tile row
+#pragma unroll 4
+        for (int id = tid; id < BM * CPR; id += kThreads) {
+            const int row = id / CPR, c = id % CPR;
+            const int m = m0 + row, n = n0 + 8 * c;
+            if (m < M && n < N)
+                *reinterpret_cast<v4u*>(static_cast<uint16_t*>(y) + (int64_t)m * N + n) =
+                    *reinterpret_cast<const v4u*>(lds + row * PITCH + 16 * c);
+        }
+        return;
+    }
+    // Other outputs: straight from the accumulators, one 8-byte (bf16) or
+    // 16-byte (f32 / i32) store per four outputs when the row length allows it.
     const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -347,23 +407,25 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
 }
 
 template <int V, int BN, int BM, int WN, int WM>
-hipError_t launch_tile(const uint8_t* qx, const float* sx, const uint8_t* qw, const uint16_t* sw, void* y,
-                       int64_t M, int64_t N, int64_t K, int mode, hipStream_t st) {
-    const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+hipError_t launch_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K, int mode,
+                       hipStream_t st) {
+    const int tm = (int)((M + BM - 1) / BM);
+    int tn = 0;
+    for (int i = 0; i < sa.nseg; ++i) tn += (sa.start[i + 1] - sa.start[i] + BN - 1) / BN;
     dim3 grid((unsigned)(tm * tn)), block(kThreads);
-    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM>), grid, block, 0, st, qx, sx, qw, sw, y,
-                       (int)M, (int)N, (int)K, mode, tm, tn);
+    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM>), grid, block, 0, st, qx, sx, sa, (int)M, (int)K, mode,
+                       tm, tn);
     return hipGetLastError();
 }
 
 template <int V>
-hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const uint8_t* qw, const uint16_t* sw,
-                          void* y, int64_t M, int64_t N, int64_t K, int mode, hipStream_t st) {
+hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K,
+                          int mode, hipStream_t st) {
     switch (cfg) {
-        case kTile256x128: return launch_tile<V, 256, 128, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
-        case kTile128x128: return launch_tile<V, 128, 128, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
-        case kTile128x64: return launch_tile<V, 128, 64, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
-        case kTile128x256: return launch_tile<V, 128, 256, 2, 2>(qx, sx, qw, sw, y, M, N, K, mode, st);
+        case kTile256x128: return launch_tile<V, 256, 128, 2, 2>(qx, sx, sa, M, K, mode, st);
+        case kTile128x128: return launch_tile<V, 128, 128, 2, 2>(qx, sx, sa, M, K, mode, st);
+        case kTile128x64: return launch_tile<V, 128, 64, 2, 2>(qx, sx, sa, M, K, mode, st);
+        case kTile128x256: return launch_tile<V, 128, 256, 2, 2>(qx, sx, sa, M, K, mode, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -373,29 +435,28 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const uin
 // Tile choice (measured on the Llama-8B projections at 512 and 1024 tokens):
 // 128 x 128 once it yields three quarters of a workgroup per CU, else
 // 128 x 64 to keep every CU busy.  The 256-row tiles need more load bandwidth
-// per CU than the 64-byte-per-clock vector memory path sustains next to the
-// LDS traffic, and lose on every shape measured.
-int large_tile_config(int64_t M, int64_t N) {
+// per CU than the vector memory path sustains next to the LDS traffic, and
+// lose on every shape measured.  Block FP8 scales every stage's partial
+// products on the vector ALUs; its smaller wave tile measured fastest.
+int large_tile_config(int variant, int64_t M, const SegmentArgs& sa) {
+    if (variant == VAR_FP8_BLOCK) return kTile128x64;
+    int64_t panels = 0;
+    for (int i = 0; i < sa.nseg; ++i) panels += (sa.start[i + 1] - sa.start[i] + 127) / 128;
     const int64_t cus = 256;
-    if (((M + 127) / 128) * ((N + 127) / 128) >= cus * 3 / 4) return kTile128x128;
+    if (((M + 127) / 128) * panels >= cus * 3 / 4) return kTile128x128;
     return kTile128x64;
 }
 
-hipError_t launch_gemm_large_cfg(int cfg, int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
-                                 const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
-                                 hipStream_t st) {
-    if (variant == VAR_INT8) return launch_variant<VAR_INT8>(cfg, qx, sx, qw, sw, y, M, N, K, mode, st);
-    if (variant == VAR_FP8_ROW) return launch_variant<VAR_FP8_ROW>(cfg, qx, sx, qw, sw, y, M, N, K, mode, st);
-    return launch_variant<VAR_FP8_BLOCK>(cfg, qx, sx, qw, sw, y, M, N, K, mode, st);
+hipError_t launch_gemm_large_cfg(int cfg, int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa,
+                                 int64_t M, int64_t K, int mode, hipStream_t st) {
+    if (variant == VAR_INT8) return launch_variant<VAR_INT8>(cfg, qx, sx, sa, M, K, mode, st);
+    if (variant == VAR_FP8_ROW) return launch_variant<VAR_FP8_ROW>(cfg, qx, sx, sa, M, K, mode, st);
+    return launch_variant<VAR_FP8_BLOCK>(cfg, qx, sx, sa, M, K, mode, st);
 }
 
-hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
-                             const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
-                             hipStream_t st) {
-    // block FP8 scales every stage's partial products on the vector ALUs; the
-    // smaller wave tile keeps those registers in budget and measured fastest
-    const int cfg = variant == VAR_FP8_BLOCK ? kTile128x64 : large_tile_config(M, N);
-    return launch_gemm_large_cfg(cfg, variant, qx, sx, qw, sw, y, M, N, K, mode, st);
+hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
+                             int64_t K, int mode, hipStream_t st) {
+    return launch_gemm_large_cfg(large_tile_config(variant, M, sa), variant, qx, sx, sa, M, K, mode, st);
 }
 
 }  // namespace qlin

@@ -75,9 +75,11 @@ qlin_status run_product(int variant, const void* q_x, const float* s_x, const vo
     hipError_t e;
     if (p == QLIN_PATH_GEMV) e = qlin::launch_gemv(variant, qx, s_x, qw, s_w, y, N, K, (int)out, stream);
     else if (p == QLIN_PATH_SMALL) e = qlin::launch_gemm_small(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
-    else if (p == QLIN_PATH_LARGE) e = qlin::launch_gemm_large(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
-    else e = qlin::launch_gemm_large_cfg((int)p - (int)QLIN_PATH_LARGE_256X128, variant, qx, s_x, qw, s_w, y, M, N, K,
-                                         (int)out, stream);
+    else if (p == QLIN_PATH_LARGE)
+        e = qlin::launch_gemm_large(variant, qx, s_x, qlin::one_segment(qw, s_w, y, N), M, K, (int)out, stream);
+    else
+        e = qlin::launch_gemm_large_cfg((int)p - (int)QLIN_PATH_LARGE_256X128, variant, qx, s_x,
+                                        qlin::one_segment(qw, s_w, y, N), M, K, (int)out, stream);
     return hip_status(e);
 }
 
@@ -156,28 +158,31 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
     if (st != QLIN_OK || noop) return st;
     const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
                         : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
-    if (fused) {
-        qlin::SegmentArgs sa{};
-        int n = 0, k = 0;
-        for (int i = 0; i < nseg; ++i) {
-            if (segments[i].n == 0) continue;
-            sa.w[k] = static_cast<const uint8_t*>(segments[i].q_w);
-            sa.sw[k] = segments[i].s_w;
-            sa.y[k] = segments[i].y;
-            sa.start[k] = n;
-            n += (int)segments[i].n;
-            ++k;
-        }
-        sa.nseg = k;
-        for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
+    // the non-empty segments, packed
+    qlin::SegmentArgs sa{};
+    int n = 0, k = 0;
+    for (int i = 0; i < nseg; ++i) {
+        if (segments[i].n == 0) continue;
+        sa.w[k] = static_cast<const uint8_t*>(segments[i].q_w);
+        sa.sw[k] = segments[i].s_w;
+        sa.y[k] = segments[i].y;
+        sa.start[k] = n;
+        n += (int)segments[i].n;
+        ++k;
+    }
+    sa.nseg = k;
+    for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
+    if (fused)
         return hip_status(qlin::launch_linear_decode(variant, x, K, sa, (int)out, static_cast<uint8_t*>(q_x), s_x,
                                                      stream));
-    }
     hipError_t e;
     if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);
     else e = qlin::launch_quant_fp8(x, M, K, variant == qlin::VAR_FP8_BLOCK ? 128 : 0, static_cast<uint8_t*>(q_x),
                                     s_x, stream);
     if (e != hipSuccess) return hip_status(e);
+    if (M > 32)   // every segment in one tiled-GEMM launch
+        return hip_status(qlin::launch_gemm_large(variant, static_cast<const uint8_t*>(q_x), s_x, sa, M, K, (int)out,
+                                                  stream));
     for (int i = 0; i < nseg; ++i) {
         if (segments[i].n == 0) continue;
         const qlin_status s = run_product(variant, q_x, s_x, segments[i].q_w, segments[i].s_w, segments[i].y, M,

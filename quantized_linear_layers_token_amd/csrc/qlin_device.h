@@ -17,6 +17,18 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 enum OutMode : int { OUT_BF16 = 0, OUT_I32 = 1, OUT_F32 = 2 };
 
+// A raw buffer descriptor over [base, base + bytes): loads at offsets at or
+// past `bytes` return zero.  Arguments must be wave-uniform; they are moved to
+// scalar registers explicitly, since a descriptor that the compiler cannot
+// prove uniform gets a readfirstlane loop around every load that uses it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------

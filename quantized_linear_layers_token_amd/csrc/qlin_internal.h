@@ -29,16 +29,28 @@ hipError_t launch_gemv(int variant, const uint8_t* qx, const float* sx, const ui
 hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
                              const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
                              hipStream_t st);
+// A single product as a one-segment SegmentArgs.
+inline SegmentArgs one_segment(const uint8_t* w, const uint16_t* sw, void* y, int64_t n) {
+    SegmentArgs sa{};
+    sa.w[0] = w;
+    sa.sw[0] = sw;
+    sa.y[0] = y;
+    sa.start[0] = 0;
+    for (int i = 1; i <= kMaxSegments; ++i) sa.start[i] = (int)n;
+    sa.nseg = 1;
+    return sa;
+}
+
 // Output tiles of the tiled GEMM (weight rows x tokens), in the order of the
 // fixed-tile paths of the C ABI.
 enum LargeTile : int { kTile256x128 = 0, kTile128x128 = 1, kTile128x64 = 2, kTile128x256 = 3 };
-hipError_t launch_gemm_large_cfg(int cfg, int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
-                                 const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
-                                 hipStream_t st);
-int large_tile_config(int64_t M, int64_t N);
-hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
-                             const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
-                             hipStream_t st);
+// The tiled GEMM over every segment of sa (one launch; a weight panel never
+// straddles two segments).  cfg: LargeTile.
+hipError_t launch_gemm_large_cfg(int cfg, int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa,
+                                 int64_t M, int64_t K, int mode, hipStream_t st);
+int large_tile_config(int variant, int64_t M, const SegmentArgs& sa);
+hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
+                             int64_t K, int mode, hipStream_t st);
 
 hipError_t launch_linear_decode(int variant, const uint16_t* x, int64_t K, const SegmentArgs& sa, int mode,
                                 uint8_t* qx, float* sx, hipStream_t st);

@@ -75,6 +75,8 @@ CASES = [
     (1, 1152, [256, 384, 128, 640]),        # four segments, ragged widths
     (3, 1024, [256, 128]),                  # staged path (small M)
     (40, 512, [384]),                       # staged path (tiled GEMM)
+    (64, 1024, [384, 128, 640]),            # three segments in one tiled-GEMM launch
+    (300, 512, [1024, 256, 256]),           # q, k, v shaped, several token tiles
 ]
 
 
@@ -134,3 +136,20 @@ def test_linear_long_k_uses_staging():
     qx_ref, sx_ref = O.quant_act_int8(x)
     assert np.array_equal(qx.view(np.int8), qx_ref)
     assert np.array_equal(ys[0], O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R])
+def test_linear_ragged_segments_tiled(scheme):
+    # segment widths that are not multiples of any tile edge: every weight
+    # panel stays inside its segment, every output row lands in its own buffer
+    M, K, ns = 100, 528, [200, 72, 300, 1]
+    x = W.x_bf16(7600, M, K)
+    segs = make_segments(scheme, 7610, ns, K)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
+    ys, _, _ = run_linear(scheme, x, segs, F32 if scheme == FP8R else I32, True)
+    for (qw, sw), y in zip(segs, ys):
+        if scheme == W8A8:
+            assert np.array_equal(y, O.contract_int8(qx_ref, qw))
+        else:
+            ye = exact(scheme, qx_ref, sx_ref, qw, sw)
+            assert np.max(np.abs(y - ye)) <= 4e-3 * np.max(np.abs(ye))
