@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--quick", action="store_true", help="headline only (no secondary sweeps, no CPU baseline)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU-oracle sample")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="for hardware-counter runs: a 1 GiB copy (counter calibration), then two eager "
+                         "decode steps; prints no JSON")
     return ap.parse_args()
 
 
@@ -301,6 +304,25 @@ def cpu_baseline(torch, W, bufs, budget_s):
 
 # ---------------------------------------------------------------------------
 
+def measured_traffic():
+    """HBM bytes per fused decode launch from the committed counter summary
+    (profiles/linear_decode_int8_llama8b_traffic.json), or None when the
+    kernel's sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "linear_decode_int8_llama8b_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        for name, digest in rec["sources_sha256"].items():
+            src = os.path.join(ROOT, "quantized_linear_layers_token_amd", "csrc", name)
+            with open(src, "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -322,6 +344,20 @@ def main():
     F, L, G, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape = build_decode(
         torch, Q, W, W.LLAMA_8B_LAYERS, dev)
     torch.cuda.synchronize()
+    if args.pmc_workload:
+        # calibration: a plain copy of known size (1 GiB read + 1 GiB written),
+        # then the decode step's 128 launches, eagerly so each is its own dispatch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            F.run()
+        torch.cuda.synchronize()
+        log(f"pmc workload done: copy 1 GiB x2, decode launches {len(F.calls)} x2, "
+            f"algorithmic bytes per step {fused_step_bytes}")
+        return
     step = capture(torch, F.run, use_graph)
     for _ in range(args.warmup):
         step()
@@ -342,7 +378,8 @@ def main():
     bytes_per_launch = fused_step_bytes / n_launch
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "kernel": "linear_decode_kernel<VAR_INT8,...> (qlin_linear, M=1)",
                 "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 3),
                 "launches": n_launch}

@@ -7,15 +7,15 @@
  *
  *   W8A8 int8   -- "Llama 3.1 8B Instruct W8A8" model card, intro and section
  *                  "Loading": int8 weights with one bf16 scale per output row,
- *                  inputs rounded to int8 one token at a time, int8 products
- *                  summed in int32.
+ *                  activations quantized to int8 per token, int8
+ *                  products accumulated in int32.
  *   FP8 rowwise -- "Llama 3.1 8B Instruct FP8" page intro and the
  *                  "Meta-Llama-3.1-8B-Instruct-FP8-dynamic" README ("Model
  *                  Optimizations", "Creation"): E4M3 weights with one scale
  *                  per output channel, per-token dynamic E4M3 inputs.
  *   FP8 block   -- "Qwen3 8B FP8" model card, intro and "Loading": E4M3
  *                  weights with one bf16 scale per 128x128 block (a
- *                  multiplier), inputs rounded to E4M3 128 at a time; widths
+ *                  multiplier), activations quantized to E4M3 in groups of 128; widths
  *                  are multiples of 128.  Per K block kb:
  *                  y[m, n] = sum_kb s_x[m, kb] * s_w[n/128, kb] * P_kb[m, n].
  *
@@ -72,9 +72,9 @@ typedef enum qlin_out {
 } qlin_out;
 
 /* Kernel regime.  AUTO follows the pages' split ("Loading" sections of the
- * W8A8 and Qwen3 model cards): one row -> a kernel that reads each weight
- * byte once; up to 32 rows -> matrix cores streaming the weights; longer
- * inputs -> a tiled matrix-core GEMM.  The other values force one kernel at
+ * W8A8 and Qwen3 model cards): a single row -> a kernel touching every
+ * weight byte exactly once; at most 32 rows -> matrix cores streaming the
+ * weights; more rows -> a tiled matrix-core GEMM.  The other values force one kernel at
  * any M (for testing each kernel outside its default regime). */
 typedef enum qlin_path {
     QLIN_PATH_AUTO = 0,
@@ -92,8 +92,8 @@ typedef enum qlin_path {
 /* Dynamic activation quantizers                                          */
 /* ---------------------------------------------------------------------- */
 
-/* Per-token int8 quantization (W8A8 model card, intro and "Loading": inputs
- * rounded to int8 a token at a time).  For each row m of x (bf16 [M, K]):
+/* Per-token int8 quantization (W8A8 model card, intro and "Loading": each
+ * token of the input gets its own int8 scale).  For each row m of x (bf16 [M, K]):
  *   a = max_k |x[m,k]|;  s[m] = fl32(a / 127);  inv = fl32(127 / a) (0 if a == 0)
  *   q[m,k] = clamp(round_half_even(fl32(x[m,k] * inv)), -127, 127)
  * q: int8 [M, K] (written), s: f32 [M] (written).  Non-finite inputs and rows
@@ -118,8 +118,8 @@ qlin_status qlin_quant_act_fp8(const uint16_t* x, int64_t M, int64_t K, int32_t 
 /* Products                                                               */
 /* ---------------------------------------------------------------------- */
 
-/* One-token W8A8 product (M = 1; W8A8 model card, "Loading": one row in a
- * kernel that reads each byte once).
+/* One-token W8A8 product (M = 1; W8A8 model card, "Loading": a single row
+ * is served by a kernel touching every weight byte exactly once).
  *   q_x int8 [K], s_x f32 [1], q_w int8 [N, K], s_w bf16 [N], y [N].
  *   acc[n] = sum_k q_x[k] q_w[n,k] (exact int32);
  *   BF16/F32: y[n] = fl32(acc) * fl32(s_x * s_w[n]), rounded to bf16 for BF16;

@@ -1,6 +1,6 @@
-// Long-input products on the matrix cores (W8A8 model card, "Loading": longer
-// inputs rounded a row at a time and multiplied in int8, summing in int32;
-// Qwen3 8B FP8 card, "Loading": block-scaled FP8 product).
+// Long-input products on the matrix cores (W8A8 model card, "Loading": inputs
+// of more than 32 rows are quantized per row and multiplied in int8 with int32
+// accumulation; Qwen3 8B FP8 card, "Loading": block-scaled FP8 product).
 //
 // Tiled GEMM, both operands K-contiguous.  Output tile = BN weight rows x BM
 // tokens, 256 threads = 4 wavefronts in a WN x WM grid; a wave owns a

@@ -1,5 +1,5 @@
 // Products for up to 32 tokens on the matrix cores (W8A8 model card and Qwen3
-// 8B FP8 card, "Loading": up to 32 rows on the matrix units).
+// 8B FP8 card, "Loading": inputs of at most 32 rows go to the matrix units).
 //
 // The weights dominate the traffic (arithmetic intensity <= 2M ops/byte), so
 // the kernel is a weight stream: every weight byte is loaded from HBM once,

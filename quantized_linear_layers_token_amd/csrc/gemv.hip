@@ -1,7 +1,8 @@
 // One-token products (M = 1): each weight byte is read from HBM exactly once.
 //
 // W8A8 model card, "Loading" (and the Qwen3 8B FP8 card's "Loading" for the
-// FP8 weights): one row in a kernel that reads each byte once.
+// FP8 weights): a single input row is served by a kernel that touches every
+// weight byte exactly once.
 //
 // Layout of the work: a wavefront owns R consecutive weight rows.  Lane l of
 // the wave reads bytes [1024 j + 16 l, 1024 j + 16 l + 16) of each row for

@@ -3,7 +3,7 @@
 // gate/up) are served by the same launch and the same activation rounding.
 //
 // The activation row is quantized cooperatively by every workgroup (W8A8 model
-// card, intro: inputs rounded to int8 one token at a time; FP8-dynamic README,
+// card, intro: activations quantized to int8 per token; FP8-dynamic README,
 // "Creation": per-token dynamic E4M3; Qwen3 8B FP8 card, "Loading": E4M3 per
 // 128 inputs): 256 threads load the bf16 row once, reduce the absmax (DPP
 // inside a wavefront, LDS across the four), round into an LDS copy of the
