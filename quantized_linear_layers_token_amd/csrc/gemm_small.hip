@@ -11,8 +11,8 @@
 //   MFMA      = A: 16 weight rows x 128 bytes of K, B: 128 bytes of K x 16
 //               tokens, C[n][m] (4 rows of one token column per lane).
 //               int8: two v_mfma_i32_16x16x64_i8 per step; E4M3: one
-//               v_mfma_f32_16x16x128_f8f6f4 per step.  Lane l supplies the 32
-//               contiguous bytes [32 (l/16), 32 (l/16) + 32) of the step for
+//               v_mfma_f32_16x16x128_f8f6f4 per step.  Lane l supplies bytes
+//               [16 (l/16), +16) and [64 + 16 (l/16), +16) of the step for
 //               row (or token) l % 16 of both operands; since both operands
 //               use the same byte-to-slot assignment the contraction is
 //               unchanged by it.
@@ -23,6 +23,8 @@
 //               weight scales, per-128-input activation scales).
 //   split-K   = the NW partial tiles are summed through LDS, then the scale
 //               epilogue writes y.
+#include <type_traits>
+
 #include "qlin_device.h"
 #include "qlin_internal.h"
 
@@ -30,162 +32,228 @@ namespace qlin {
 
 namespace {
 
-constexpr int kSmallUnroll = 4;     // K steps whose loads are issued together
+template <int U> using IC = std::integral_constant<int, U>;
+constexpr int kSmallBatch = 2;      // K steps per load batch for 64-row tiles (two batches in flight)
+constexpr int kOOB = 0x40000000;    // an offset past every descriptor's range: reads zero
+constexpr int kAuxStream = 2;       // buffer-load cache policy: streaming (slc)
 
 template <int V> struct SmallAcc { typedef v4i T; };
 template <> struct SmallAcc<VAR_FP8_ROW> { typedef v4f T; };
 template <> struct SmallAcc<VAR_FP8_BLOCK> { typedef v4f T; };
 
-template <int V, int MT, int NW>
+template <int V, int MT, int NW, int RT>
 __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
-    const uint8_t* __restrict__ qx, const float* __restrict__ sx,
-    const uint8_t* __restrict__ qw, const uint16_t* __restrict__ sw,
-    void* __restrict__ y, int M, int N, int K, int mode) {
+    const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode) {
     typedef typename SmallAcc<V>::T Acc;
-    __shared__ Acc red[NW][MT][kWave];
+    __shared__ Acc red[NW][RT * MT][kWave];
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
-    const int r16 = lane & 15;           // weight row / token column within the tile
-    const int grp = lane >> 4;           // which 32-byte quarter of a K step
-    const int n0 = blockIdx.x * 16;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15;           // weight row / token column within a 16 x 16 MFMA tile
+    const int grp = lane >> 4;           // which 16-byte piece of each 64-byte half of a K step
+
+    // tiles of 16 RT weight rows (RT MFMA tiles sharing the token loads) are numbered across the segments (q, k, v or gate, up
+    // sharing one input); a tile never straddles two segments
+    constexpr int TR = 16 * RT;
+    int tile = blockIdx.x, seg = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < kMaxSegments; ++i) {
+        const int nt = (sa.start[i + 1] - sa.start[i] + TR - 1) / TR;
+        if (seg == i && i + 1 < sa.nseg && tile >= nt) {
+            tile -= nt;
+            seg = i + 1;
+        }
+    }
+    const uint8_t* __restrict__ qw = sa.w[seg];
+    const uint16_t* __restrict__ sw = sa.sw[seg];
+    void* __restrict__ y = sa.y[seg];
+    const int N = sa.start[seg + 1] - sa.start[seg];
+    const int n0 = __builtin_amdgcn_readfirstlane(tile * TR);
 
     const int nsteps = (K + 127) >> 7;
     const int per = (nsteps + NW - 1) / NW;
     const int s_begin = wave * per;
     const int s_end = min(nsteps, s_begin + per);
 
-    // Rows past N or tokens past M re-read a valid row; their outputs are
-    // never stored, and A rows / B columns do not mix in the MFMA.
-    const int nrow = min(n0 + r16, N - 1);
-    const uint8_t* wbase = qw + (int64_t)nrow * K + grp * 32;
-    const uint8_t* xbase[MT];
+    // Buffer descriptors over the tile's weight rows and over the M token
+    // rows: rows past N or M, K past the end and steps past the wave's range
+    // read as zero (an out-of-range offset), with no select after the load.
+    const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(TR, N - n0) * K);
+    const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(qx, M * K);
+    // Lane (r16, grp) takes bytes [16 grp, 16 grp + 16) and [64 + 16 grp, ...)
+    // of each 128-byte step, so one load instruction covers one contiguous
+    // 64-byte piece of each of 16 rows.  Both operands use the same
+    // assignment, so the contraction is unchanged by it.  The RT weight tiles
+    // of a wavefront share its token registers.
+    const int woff = r16 * K + grp * 16;
+    int xoff[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) xbase[t] = qx + (int64_t)min(t * 16 + r16, M - 1) * K + grp * 32;
+    for (int t = 0; t < MT; ++t) xoff[t] = (t * 16 + r16 < M) ? (t * 16 + r16) * K + grp * 16 : kOOB;
 
     const int kbs = K >> 7;
-    const uint16_t* swblk = sw + (int64_t)(n0 >> 7) * kbs;  // block FP8: this tile's row block
+    const uint16_t* swblk = sw + (int64_t)(n0 >> 7) * kbs;  // block FP8: the tile's 128-row block
 
-    Acc acc[MT];
+    Acc acc[RT][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = Acc{0, 0, 0, 0};
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = Acc{0, 0, 0, 0};
 
-    for (int s0 = s_begin; s0 < s_end; s0 += kSmallUnroll) {
-        v4u wa[kSmallUnroll][2], xa[kSmallUnroll][MT][2];
-        float fx[kSmallUnroll][MT], fw[kSmallUnroll];
+    // Batches of kSmallBatch K steps, double-buffered: batch b + 1 is loaded
+    // while batch b is multiplied, so a wavefront keeps two batches of loads
+    // in flight.  Loads past the wavefront's steps read zero.
+    constexpr int U = RT == 1 ? 2 * kSmallBatch : kSmallBatch;   // same register budget either way
+    v4u wa[2][U][RT][2], xa[2][U][MT][2];
+    float fx[2][U][MT], fw[2][U];
+    auto issue = [&](auto bufc, int s0) {
+        constexpr int bi = decltype(bufc)::value;
 #pragma unroll
-        for (int u = 0; u < kSmallUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int s = s0 + u;
-            const int k = s * 128 + grp * 32;
+            const int k = s * 128 + grp * 16;
             const bool ok0 = (s < s_end) && (k < K);
-            const bool ok1 = (s < s_end) && (k + 16 < K);
-            const v4u* wp = reinterpret_cast<const v4u*>(wbase + (int64_t)s * 128);
-            wa[u][0] = ok0 ? __builtin_nontemporal_load(wp) : v4u{0, 0, 0, 0};
-            wa[u][1] = ok1 ? __builtin_nontemporal_load(wp + 1) : v4u{0, 0, 0, 0};
+            const bool ok1 = (s < s_end) && (k + 64 < K);
+            // weights stream once: non-temporal
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int o = woff + r * 16 * K + s * 128;
+                wa[bi][u][r][0] = __builtin_amdgcn_raw_buffer_load_b128(dw, ok0 ? o : kOOB, 0, kAuxStream);
+                wa[bi][u][r][1] = __builtin_amdgcn_raw_buffer_load_b128(dw, ok1 ? o + 64 : kOOB, 0, kAuxStream);
+            }
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                const v4u* xp = reinterpret_cast<const v4u*>(xbase[t] + (int64_t)s * 128);
-                xa[u][t][0] = ok0 ? xp[0] : v4u{0, 0, 0, 0};
-                xa[u][t][1] = ok1 ? xp[1] : v4u{0, 0, 0, 0};
+                xa[bi][u][t][0] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok0 ? xoff[t] + s * 128 : kOOB, 0, 0);
+                xa[bi][u][t][1] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok1 ? xoff[t] + s * 128 + 64 : kOOB, 0, 0);
             }
             if constexpr (V == VAR_FP8_BLOCK) {
                 const int sb = min(s, s_end - 1);
-                fw[u] = bf16_lo(swblk[sb]);
+                fw[bi][u] = bf16_lo(swblk[sb]);
 #pragma unroll
-                for (int t = 0; t < MT; ++t) fx[u][t] = sx[(int64_t)min(t * 16 + r16, M - 1) * kbs + sb];
+                for (int t = 0; t < MT; ++t) fx[bi][u][t] = sx[(int64_t)min(t * 16 + r16, M - 1) * kbs + sb];
             }
         }
+    };
+    auto compute = [&](auto bufc, int s0) {
+        constexpr int bi = decltype(bufc)::value;
 #pragma unroll
-        for (int u = 0; u < kSmallUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                if constexpr (V == VAR_INT8) {
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                        __builtin_bit_cast(v4i, wa[u][0]), __builtin_bit_cast(v4i, xa[u][t][0]), acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                        __builtin_bit_cast(v4i, wa[u][1]), __builtin_bit_cast(v4i, xa[u][t][1]), acc[t], 0, 0, 0);
-                } else {
-                    const v8i a = v8i{(int)wa[u][0].x, (int)wa[u][0].y, (int)wa[u][0].z, (int)wa[u][0].w,
-                                      (int)wa[u][1].x, (int)wa[u][1].y, (int)wa[u][1].z, (int)wa[u][1].w};
-                    const v8i b = v8i{(int)xa[u][t][0].x, (int)xa[u][t][0].y, (int)xa[u][t][0].z, (int)xa[u][t][0].w,
-                                      (int)xa[u][t][1].x, (int)xa[u][t][1].y, (int)xa[u][t][1].z, (int)xa[u][t][1].w};
-                    if constexpr (V == VAR_FP8_ROW) {
-                        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[t], 0, 0, 0, 0, 0, 0);
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const v4u w0 = wa[bi][u][r][0], w1 = wa[bi][u][r][1], x0 = xa[bi][u][t][0], x1 = xa[bi][u][t][1];
+                    if constexpr (V == VAR_INT8) {
+                        acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, w0),
+                                                                          __builtin_bit_cast(v4i, x0), acc[r][t], 0, 0, 0);
+                        acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, w1),
+                                                                          __builtin_bit_cast(v4i, x1), acc[r][t], 0, 0, 0);
                     } else {
-                        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                        if (s0 + u < s_end) {
-                            const float f = fx[u][t] * fw[u];
-                            acc[t].x = __builtin_fmaf(p.x, f, acc[t].x);
-                            acc[t].y = __builtin_fmaf(p.y, f, acc[t].y);
-                            acc[t].z = __builtin_fmaf(p.z, f, acc[t].z);
-                            acc[t].w = __builtin_fmaf(p.w, f, acc[t].w);
+                        const v8i a = v8i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+                        const v8i b = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                        if constexpr (V == VAR_FP8_ROW) {
+                            acc[r][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[r][t], 0, 0, 0, 0, 0, 0);
+                        } else {
+                            const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            if (s0 + u < s_end) {
+                                const float f = fx[bi][u][t] * fw[bi][u];
+                                acc[r][t].x = __builtin_fmaf(p.x, f, acc[r][t].x);
+                                acc[r][t].y = __builtin_fmaf(p.y, f, acc[r][t].y);
+                                acc[r][t].z = __builtin_fmaf(p.z, f, acc[r][t].z);
+                                acc[r][t].w = __builtin_fmaf(p.w, f, acc[r][t].w);
+                            }
                         }
                     }
                 }
-            }
         }
+    };
+
+    issue(IC<0>{}, s_begin);
+    int s0 = s_begin;
+    for (; s0 + U < s_end; s0 += 2 * U) {                 // at least two batches left
+        issue(IC<1>{}, s0 + U);
+        __builtin_amdgcn_sched_barrier(0);                 // both batches in flight before the first wait
+        compute(IC<0>{}, s0);
+        issue(IC<0>{}, s0 + 2 * U);                        // possibly all past the end: zeros, never used
+        __builtin_amdgcn_sched_barrier(0);
+        compute(IC<1>{}, s0 + U);
     }
+    if (s0 < s_end) compute(IC<0>{}, s0);
 
 #pragma unroll
-    for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[wave][r * MT + t][lane] = acc[r][t];
     __syncthreads();
 
-    // Sum the NW partial tiles; thread (t, lane) finishes token column t*16 + lane%16.
-    if (threadIdx.x < MT * kWave) {
-        const int t = threadIdx.x >> 6;
-        Acc sum = red[0][t][lane];
+    // Sum the NW partial tiles.  Item (r, t, l): weight rows n0 + 16 r + 4 (l / 16)
+    // .. + 3 of token m = 16 t + l % 16.
+    for (int it = tid; it < RT * MT * kWave; it += NW * kWave) {
+        const int rt = it / kWave, l = it % kWave;
+        const int r = rt / MT, t = rt % MT;
+        Acc sum = red[0][rt][l];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) sum += red[w][t][lane];
-        const int m = t * 16 + r16;
+        for (int w = 1; w < NW; ++w) sum += red[w][rt][l];
+        const int m = t * 16 + (l & 15);
         if (m < M) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = n0 + grp * 4 + r;
+            for (int e = 0; e < 4; ++e) {
+                const int n = n0 + 16 * r + (l >> 4) * 4 + e;
                 if (n < N) {
                     const int64_t idx = (int64_t)m * N + n;
-                    if constexpr (V == VAR_INT8) store_rowwise_i32acc(y, idx, sum[r], sx[m], sw[n], mode);
-                    else if constexpr (V == VAR_FP8_ROW) store_f32(y, idx, sum[r] * (sx[m] * bf16_lo(sw[n])), mode);
-                    else store_f32(y, idx, sum[r], mode);
+                    if constexpr (V == VAR_INT8) store_rowwise_i32acc(y, idx, sum[e], sx[m], sw[n], mode);
+                    else if constexpr (V == VAR_FP8_ROW) store_f32(y, idx, sum[e] * (sx[m] * bf16_lo(sw[n])), mode);
+                    else store_f32(y, idx, sum[e], mode);
                 }
             }
         }
     }
 }
 
-template <int V, int MT>
-void launch_mt(int nw, dim3 grid, hipStream_t st, const uint8_t* qx, const float* sx, const uint8_t* qw,
-               const uint16_t* sw, void* y, int M, int N, int K, int mode) {
-    if (nw >= 16)
-        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 16>), grid, dim3(16 * 64), 0, st, qx, sx, qw, sw, y, M, N, K, mode);
-    else if (nw >= 8)
-        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 8>), grid, dim3(8 * 64), 0, st, qx, sx, qw, sw, y, M, N, K, mode);
+template <int V, int MT, int RT>
+void launch_mt(int nw, dim3 grid, hipStream_t st, const uint8_t* qx, const float* sx, const SegmentArgs& sa,
+               int M, int K, int mode) {
+    if (nw >= 8)
+        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 8, RT>), grid, dim3(8 * 64), 0, st, qx, sx, sa, M, K, mode);
     else
-        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 4>), grid, dim3(4 * 64), 0, st, qx, sx, qw, sw, y, M, N, K, mode);
+        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 4, RT>), grid, dim3(4 * 64), 0, st, qx, sx, sa, M, K, mode);
+}
+
+int64_t small_tiles(const SegmentArgs& sa, int rows) {
+    int64_t tiles = 0;
+    for (int i = 0; i < sa.nseg; ++i) tiles += (sa.start[i + 1] - sa.start[i] + rows - 1) / rows;
+    return tiles;
 }
 
 }  // namespace
 
-// K-split depth: enough waves for >= 2048 in flight, bounded by the K steps.
+// K-split depth: 4 wavefronts for K up to 4 Ki (each keeps its eight steps in
+// flight as four batches), else 8.
 int small_waves_per_tile(int64_t N, int64_t K) {
-    const int64_t tiles = (N + 15) / 16;
-    const int64_t steps = (K + 127) / 128;
-    int nw = 4;
-    while (nw < 16 && tiles * nw < 2048 && steps >= 2 * nw * kSmallUnroll) nw *= 2;
-    return nw;
+    (void)N;
+    return K <= 4096 ? 4 : 8;
 }
 
-hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
-                             const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
-                             hipStream_t st) {
-    dim3 grid((unsigned)((N + 15) / 16));
-    const int nw = small_waves_per_tile(N, K);
-    const int m = (int)M, n = (int)N, k = (int)K;
+hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
+                             int64_t K, int mode, hipStream_t st) {
+    // 64-row tiles share each token load four ways, but only pay off with at
+    // least a workgroup per CU for every 64 rows (the wide gate/up launch)
+    const bool wide = small_tiles(sa, 64) >= 256;
+    const int64_t tiles = small_tiles(sa, wide ? 64 : 16);
+    dim3 grid((unsigned)tiles);
+    const int nw = small_waves_per_tile(tiles, K);
+    const int m = (int)M, k = (int)K;
     const bool two = M > 16;
-#define QLIN_SMALL(VV)                                                          \
-    do {                                                                        \
-        if (two) launch_mt<VV, 2>(nw, grid, st, qx, sx, qw, sw, y, m, n, k, mode); \
-        else launch_mt<VV, 1>(nw, grid, st, qx, sx, qw, sw, y, m, n, k, mode);     \
+#define QLIN_SMALL(VV)                                                                \
+    do {                                                                              \
+        if (wide) {                                                                   \
+            if (two) launch_mt<VV, 2, 4>(nw, grid, st, qx, sx, sa, m, k, mode);       \
+            else launch_mt<VV, 1, 4>(nw, grid, st, qx, sx, sa, m, k, mode);           \
+        } else {                                                                      \
+            if (two) launch_mt<VV, 2, 1>(nw, grid, st, qx, sx, sa, m, k, mode);       \
+            else launch_mt<VV, 1, 1>(nw, grid, st, qx, sx, sa, m, k, mode);           \
+        }                                                                             \
     } while (0)
     if (variant == VAR_INT8) QLIN_SMALL(VAR_INT8);
     else if (variant == VAR_FP8_ROW) QLIN_SMALL(VAR_FP8_ROW);

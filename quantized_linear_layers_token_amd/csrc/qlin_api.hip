@@ -74,7 +74,8 @@ qlin_status run_product(int variant, const void* q_x, const float* s_x, const vo
     if (p == QLIN_PATH_AUTO) p = (M == 1) ? QLIN_PATH_GEMV : (M <= 32 ? QLIN_PATH_SMALL : QLIN_PATH_LARGE);
     hipError_t e;
     if (p == QLIN_PATH_GEMV) e = qlin::launch_gemv(variant, qx, s_x, qw, s_w, y, N, K, (int)out, stream);
-    else if (p == QLIN_PATH_SMALL) e = qlin::launch_gemm_small(variant, qx, s_x, qw, s_w, y, M, N, K, (int)out, stream);
+    else if (p == QLIN_PATH_SMALL)
+        e = qlin::launch_gemm_small(variant, qx, s_x, qlin::one_segment(qw, s_w, y, N), M, K, (int)out, stream);
     else if (p == QLIN_PATH_LARGE)
         e = qlin::launch_gemm_large(variant, qx, s_x, qlin::one_segment(qw, s_w, y, N), M, K, (int)out, stream);
     else
@@ -182,6 +183,9 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
     if (e != hipSuccess) return hip_status(e);
     if (M > 32)   // every segment in one tiled-GEMM launch
         return hip_status(qlin::launch_gemm_large(variant, static_cast<const uint8_t*>(q_x), s_x, sa, M, K, (int)out,
+                                                  stream));
+    if (M > 1)    // every segment in one small-M launch
+        return hip_status(qlin::launch_gemm_small(variant, static_cast<const uint8_t*>(q_x), s_x, sa, M, K, (int)out,
                                                   stream));
     for (int i = 0; i < nseg; ++i) {
         if (segments[i].n == 0) continue;

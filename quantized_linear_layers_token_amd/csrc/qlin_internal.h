@@ -26,9 +26,10 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int group, 
 
 hipError_t launch_gemv(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw, const uint16_t* sw,
                        void* y, int64_t N, int64_t K, int mode, hipStream_t st);
-hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const uint8_t* qw,
-                             const uint16_t* sw, void* y, int64_t M, int64_t N, int64_t K, int mode,
-                             hipStream_t st);
+// Small-M product over every segment of sa in one launch (16-row tiles never
+// straddle two segments).
+hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
+                             int64_t K, int mode, hipStream_t st);
 // A single product as a one-segment SegmentArgs.
 inline SegmentArgs one_segment(const uint8_t* w, const uint16_t* sw, void* y, int64_t n) {
     SegmentArgs sa{};
