@@ -47,6 +47,7 @@ __all__ = [
     "rescale_rowwise", "rescale_block",
     "linear_w8a8", "linear_fp8_rowwise", "linear_fp8_block",
     "epilogue_f32_order",
+    "dequantize_weights", "linear_weight_only",
 ]
 
 # Largest code magnitude of each target format.
@@ -336,3 +337,42 @@ def linear_fp8_block(x_bits, q_w, s_w_bits):
     P = contract_e4m3_blocks(q_x, q_w)
     y = rescale_block(P, s_x, s_w_bits)
     return round_to_bf16_bits(y), y, q_x, s_x
+
+
+# --------------------------------------------------------------------------
+# Weight-only ("equivalent") numerics
+# --------------------------------------------------------------------------
+
+def dequantize_weights(q_w, s_w_bits, scheme: str, block: int = 128) -> np.ndarray:
+    """W[n, k] = s_w * value(q_w[n, k]) in fp64 (exact: a bf16 scale times an
+    int8 or E4M3 value has at most 8 + 8 significant bits).  scheme: "int8",
+    "fp8_rowwise" (s_w [N]) or "fp8_block" (s_w [N/128, K/128], a multiplier;
+    Qwen3 8B FP8 card, intro)."""
+    if scheme == "int8":
+        v = np.asarray(q_w, dtype=np.int8).astype(np.float64)
+    else:
+        v = e4m3_decode(q_w)
+    N, K = v.shape
+    sw = bf16_bits_to_f64(s_w_bits)
+    if scheme == "fp8_block":
+        assert sw.shape == ((N + block - 1) // block, (K + block - 1) // block)
+        full = np.repeat(np.repeat(sw, block, axis=0)[:N], block, axis=1)[:, :K]
+        return v * full
+    return v * sw[:, None]
+
+
+def linear_weight_only(x_bits, q_w, s_w_bits, scheme: str):
+    """Weight-only ("equivalent") numerics: the input is never rounded; the
+    product uses the bf16 activations and the dequantized weights
+    (W8A8 model card and Qwen3 8B FP8 card, "Against bf16": the "equivalent"
+    mode keeps the input unrounded; "Loading": the numerics option).
+
+        y_exact[m, n] = sum_k x[m, k] * W[n, k],   W = dequantize_weights(...)
+
+    The products are exact in fp64 (8 + 16 significant bits); the fp64 sum is
+    within K * 2**-53 of the exact sum, far below the bf16 output's resolution.
+    Returns (y_bits [M, N] bf16_rne(y_exact), y_exact [M, N] fp64)."""
+    x = bf16_bits_to_f64(x_bits)
+    w = dequantize_weights(q_w, s_w_bits, scheme)
+    y = x @ w.T
+    return round_to_bf16_bits(y), y

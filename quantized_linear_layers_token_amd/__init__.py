@@ -66,7 +66,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m quantized_linear_layers_token_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python quantized_linear_layers_token_amd/build.py` "
             "(the HIP library is the only implementation; there is no fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():

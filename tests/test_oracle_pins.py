@@ -448,3 +448,91 @@ def test_epilogue_order_within_tolerance():
 def test_math_constants():
     assert O.Q_E4M3 == float(O.e4m3_decode(np.array([0x7E], np.uint8))[0])
     assert math.isclose(O.Q_INT8, 127.0)
+
+
+# ---------------------------------------------------------------------------
+# Weight-only ("equivalent") numerics
+# ---------------------------------------------------------------------------
+
+def _weight_only_fraction(xbits, q_w, sw_bits, scheme):
+    """Exact rational evaluation of sum_k x[m,k] * s_w * value(q_w[n,k])."""
+    M, K = xbits.shape
+    N = q_w.shape[0]
+    tab = dict(e4m3_table())                 # code -> exact value
+    out = np.zeros((M, N), dtype=object)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for k in range(K):
+                if scheme == "int8":
+                    v = Fraction(int(np.int8(q_w[n, k])))
+                else:
+                    v = tab[int(q_w[n, k])]
+                sc = bf16_value(int(sw_bits[n // 128, k // 128])) if scheme == "fp8_block" else bf16_value(int(sw_bits[n]))
+                tot += bf16_value(int(xbits[m, k])) * sc * v
+            out[m, n] = tot
+    return out
+
+
+@pytest.mark.parametrize("scheme", ["int8", "fp8_rowwise", "fp8_block"])
+def test_weight_only_fraction_bruteforce(scheme):
+    M, N, K = 2, 3 if scheme != "fp8_block" else 130, 256
+    x = W.x_bf16(900, M, K)
+    qw = W.w_int8(901, N, K) if scheme == "int8" else W.w_e4m3(901, N, K)
+    sw = W.scale_bf16(902, ((N + 127) // 128, K // 128) if scheme == "fp8_block" else (N,))
+    _, y = O.linear_weight_only(x, qw, sw, scheme)
+    cols = [0, 1, 129] if scheme == "fp8_block" else list(range(N))   # rows from both 128-row blocks
+    ref = _weight_only_fraction(x, qw[cols], sw, scheme) if scheme != "fp8_block" else None
+    if scheme == "fp8_block":
+        full = _weight_only_fraction(x, qw[: 130], sw, scheme)
+        ref = full[:, cols]
+    for m in range(M):
+        for i, n in enumerate(cols):
+            exact = float(ref[m, i])
+            assert abs(y[m, n] - exact) <= 1e-13 * max(1.0, abs(exact)), (m, n, y[m, n], exact)
+
+
+def test_weight_only_equals_w8a8_when_rounding_is_exact():
+    # x = 2**-5 * q with max|q| = 127: the per-token int8 rounding reproduces q
+    # and s exactly, so the two numerics define the same value
+    rng = np.random.default_rng(903)
+    M, N, K = 4, 96, 512
+    q = rng.integers(-127, 128, (M, K), dtype=np.int64)
+    q[:, 7] = 127
+    xbits = O.round_to_bf16_bits(q.astype(np.float64) * 2.0 ** -5)
+    qw = W.w_int8(904, N, K)
+    sw = W.scale_bf16(905, N)
+    _, y_w8a8, qx, sx, _ = O.linear_w8a8(xbits, qw, sw)
+    assert np.array_equal(qx.astype(np.int64), q) and np.all(sx == np.float32(2.0 ** -5))
+    _, y_wo = O.linear_weight_only(xbits, qw, sw, "int8")
+    assert np.allclose(y_wo, y_w8a8, rtol=1e-14, atol=0)
+
+
+def test_weight_only_equals_fp8_rowwise_when_rounding_is_exact():
+    # x = 2**-3 * (E4M3 values) with max |value| = 448: per-token FP8 rounding is exact
+    rng = np.random.default_rng(906)
+    M, N, K = 3, 64, 384
+    codes = (rng.integers(0, 0x7E, (M, K)) | (rng.integers(0, 2, (M, K)) << 7)).astype(np.uint8)
+    codes[:, 3] = 0x7E
+    xbits = O.round_to_bf16_bits(O.e4m3_decode(codes) * 2.0 ** -3)
+    qw = W.w_e4m3(907, N, K)
+    sw = W.scale_bf16(908, N)
+    _, y_fp8, qx, sx = O.linear_fp8_rowwise(xbits, qw, sw)
+    assert np.all(sx == np.float32(2.0 ** -3))
+    _, y_wo = O.linear_weight_only(xbits, qw, sw, "fp8_rowwise")
+    assert np.allclose(y_wo, y_fp8, rtol=1e-14, atol=0)
+
+
+def test_weight_only_block_reduces_to_rowwise_and_scales_exactly():
+    M, N, K = 2, 256, 384
+    x = W.x_bf16(909, M, K)
+    qw = W.w_e4m3(910, N, K)
+    row = W.scale_bf16(911, N // 128)                    # one scale per 128-row band
+    blk = np.repeat(row[:, None], K // 128, axis=1)      # equal along K
+    _, yb = O.linear_weight_only(x, qw, blk, "fp8_block")
+    _, yr = O.linear_weight_only(x, qw, np.repeat(row, 128), "fp8_rowwise")
+    assert np.allclose(yb, yr, rtol=1e-14, atol=0)
+    # power-of-two homogeneity in x is exact
+    x2 = O.round_to_bf16_bits(O.bf16_bits_to_f64(x) * 4.0)
+    _, y4 = O.linear_weight_only(x2, qw, blk, "fp8_block")
+    assert np.array_equal(y4, yb * 4.0)
