@@ -88,6 +88,13 @@ class Launcher:
                                                  None if qx is None else qx.data_ptr(),
                                                  None if sx is None else sx.data_ptr())))
 
+    def linear_weight_only(self, scheme, x, segs, out=0):
+        """segs: [(q_w, s_w, y), ...] sharing x (weight-only numerics)."""
+        M, K = x.shape
+        arr = self.Q.segments_array(segs)
+        self.keep.append(arr)
+        self.calls.append((self.L.qlin_linear_weight_only, (scheme, x.data_ptr(), M, K, arr, len(segs), out)))
+
     def gemm(self, fn, qx, sx, qw, sw, y, M, N, K, out=0, path=0):
         f = getattr(self.L, fn + "_ex")
         self.calls.append((f, (qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
@@ -160,6 +167,7 @@ def build_decode(torch, Q, W, layers, dev):
     F = Launcher(Q, torch)
     L = Launcher(Q, torch)
     G = Launcher(Q, torch)
+    WO = Launcher(Q, torch)
     gen = torch.Generator(device=dev)
     shapes = dict((n, (N, K)) for n, N, K in W.LLAMA_8B)
     bufs = []
@@ -184,6 +192,7 @@ def build_decode(torch, Q, W, layers, dev):
             step_bytes += quant_bytes(1, K)
             lw["in_" + group[0]] = (x, q, s)
             F.linear(0, x, [(lw[name][0], lw[name][1], lw[name][2]) for name in group])
+            WO.linear_weight_only(0, x, [(lw[name][0], lw[name][1], lw[name][2]) for name in group])
             fused_step_bytes += fused_bytes(K, [shapes[name][0] for name in group])
             for name in group:
                 qw, sw, y = lw[name]
@@ -195,7 +204,7 @@ def build_decode(torch, Q, W, layers, dev):
                 gemv_bytes += b
                 per_shape.setdefault(name, []).append((q, s, qw, sw, y, N, K2))
         bufs.append(lw)
-    return F, L, G, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape
+    return F, L, G, WO, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape
 
 
 def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
@@ -341,7 +350,7 @@ def main():
 
     # ---- headline: decode, M = 1, 32 distinct layers -------------------------
     log("building decode workload (32 layers, int8)")
-    F, L, G, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape = build_decode(
+    F, L, G, WO, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape = build_decode(
         torch, Q, W, W.LLAMA_8B_LAYERS, dev)
     torch.cuda.synchronize()
     if args.pmc_workload:
@@ -393,6 +402,12 @@ def main():
     gemv_only = capture(torch, G.run, use_graph)
     gemv_only()
     ms_gemv = time_events(torch, gemv_only, max(3, args.steps // 2))
+    # the same step under weight-only numerics (bf16 input never rounded)
+    wo = capture(torch, WO.run, use_graph)
+    wo()
+    ms_wo = time_events(torch, wo, max(3, args.steps // 2))
+    secondary["decode_weight_only"] = {"ms_per_step": round(ms_wo, 4),
+                                       "gbs": round(fused_step_bytes / (ms_wo * 1e-3) / 1e9, 1)}
     secondary["decode_two_kernel"] = {
         "ms_per_step": round(ms_two, 4), "gbs": round(step_bytes / (ms_two * 1e-3) / 1e9, 1),
         "gemv_only_gbs": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
@@ -419,9 +434,12 @@ def main():
         fused = [(n, N, K) for n, N, K in W.LLAMA_8B_FUSED]
         wts = {n: (W.torch_w_int8(torch, gen, N, K, dev), W.torch_scale_bf16(torch, gen, (N,), dev))
                for n, N, K in fused}
+        small_wo = {}
         for M in (4, 8, 16, 32):
             P = Launcher(Q, torch)
+            PW = Launcher(Q, torch)
             nb = 0
+            nbw = 0
             ops = 0
             keep = []
             for n, N, K in fused:
@@ -432,16 +450,24 @@ def main():
                 keep += [x, q, s, y]
                 Q.qlin_quant_act_int8(x, q, s)
                 P.gemm("qlin_gemm_w8a8", q, s, wts[n][0], wts[n][1], y, M, N, K)
+                PW.linear_weight_only(0, x, [(wts[n][0], wts[n][1], y)])
                 nb += N * K + 2 * N + M * K + 4 * M + 2 * M * N
+                nbw += N * K + 2 * N + 2 * M * K + 2 * M * N
                 ops += 2 * M * N * K
             fn = capture(torch, P.run, use_graph)
             fn()
             t = time_events(torch, fn, 10)
             small[str(M)] = {"gbs": round(nb / (t * 1e-3) / 1e9, 1), "tops": round(ops / (t * 1e-3) / 1e12, 2),
                              "us_per_layer": round(t * 1e3, 2)}
+            fw = capture(torch, PW.run, use_graph)
+            fw()
+            t = time_events(torch, fw, 10)
+            small_wo[str(M)] = {"gbs": round(nbw / (t * 1e-3) / 1e9, 1), "us_per_layer": round(t * 1e3, 2)}
             del keep
         secondary["small_m_fused_int8"] = small
+        secondary["small_m_weight_only_int8"] = small_wo
         log(f"small-M fused {small}")
+        log(f"small-M weight-only {small_wo}")
         del wts
 
         # prefill TOPS

@@ -207,11 +207,28 @@ typedef struct qlin_segment {
  * and streams its share of all segments' weight rows; q_x / s_x may be null, and
  * when given receive the codes and scale(s).  Otherwise q_x (M*K bytes) and s_x
  * ([M] or [M, K/128] f32) are required caller-owned staging buffers: one
- * quantizer launch, then one product launch per segment (regime by M).
- * The segments array is read during the call only. */
+ * quantizer launch, then one product launch covering every segment (regime by
+ * M).  The segments array is read during the call only. */
 qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
                         const qlin_segment* segments, int32_t nseg, qlin_out out,
                         void* q_x, float* s_x, hipStream_t stream);
+
+/* Weight-only ("equivalent") numerics: the input is never rounded (W8A8 model
+ * card and Qwen3 8B FP8 card, "Against bf16"; "Loading": the numerics option).
+ * For each segment, with the codes and scales of the scheme's weights:
+ *   W8A8, FP8_ROWWISE:  y[m, n] = s_w[n] * sum_k x[m, k] * q_w[n, k]
+ *   FP8_BLOCK:          y[m, n] = sum_kb s_w[n/128, kb] * sum_{k in block kb} x[m, k] * q_w[n, k]
+ * x bf16 [M, K] (16-byte aligned, K % 16 == 0; K % 128 == 0 for FP8_BLOCK),
+ * 1 <= M <= 32 (larger M: QLIN_ERR_UNSUPPORTED), segments as for qlin_linear.
+ * out: QLIN_OUT_BF16 (round to nearest even) or QLIN_OUT_F32; QLIN_OUT_I32 is
+ * QLIN_ERR_UNSUPPORTED.  Products of the bf16 inputs and the codes are exact;
+ * the sums are f32.  One launch for all segments: M == 1 with K <= 16384 streams
+ * each weight byte once on the vector ALUs; otherwise the codes are widened to
+ * bf16 in registers for the matrix cores.  Same validation, ownership and error
+ * behaviour as qlin_linear. */
+qlin_status qlin_linear_weight_only(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                                    const qlin_segment* segments, int32_t nseg, qlin_out out,
+                                    hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Helpers                                                                */

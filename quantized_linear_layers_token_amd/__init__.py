@@ -40,6 +40,7 @@ SIGNATURES = {
     "qlin_gemm_fp8_block": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _P]),
     "qlin_gemm_fp8_block_ex": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _S, _P]),
     "qlin_linear": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P, _P, _P]),
+    "qlin_linear_weight_only": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P]),
     "qlin_status_string": (ctypes.c_char_p, [_S]),
     "qlin_abi_version": (_S, []),
     "qlin_last_hip_error": (_S, []),
@@ -190,3 +191,15 @@ def qlin_linear(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=No
     arr = segments_array(segments)
     _check(_lib.qlin_linear(scheme, _ptr(x), M, K, arr, len(segments), out, _ptr(q_x), _ptr(s_x),
                             _stream(stream)), "qlin_linear")
+
+
+def qlin_linear_weight_only(scheme, x, segments, out=OUT_BF16, stream=None):
+    """Weight-only numerics: x bf16 [M, K] (M <= 32) times the dequantized
+    weights of each segment (q_w [n, K], s_w, y [M, n]); the input is not rounded."""
+    M, K = _dims2(x, "x")
+    for qw, _, _ in segments:
+        if qw.dim() != 2 or qw.shape[1] != K:
+            raise ValueError("every q_w must be [n, K]")
+    arr = segments_array(segments)
+    _check(_lib.qlin_linear_weight_only(scheme, _ptr(x), M, K, arr, len(segments), out, _stream(stream)),
+           "qlin_linear_weight_only")

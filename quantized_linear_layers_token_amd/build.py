@@ -18,7 +18,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlin.so")
 
 ARCH = "gfx950"
-SOURCES = ["quant_act.hip", "gemv.hip", "gemm_small.hip", "gemm_large.hip", "linear.hip", "qlin_api.hip"]
+SOURCES = ["quant_act.hip", "gemv.hip", "gemm_small.hip", "gemm_large.hip", "linear.hip", "weight_only.hip",
+           "qlin_api.hip"]
 HEADERS = ["qlin_device.h", "qlin_internal.h"]
 
 # Never fast-math, never flush denormals: the quantizers are bit-exact against

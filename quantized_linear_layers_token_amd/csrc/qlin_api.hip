@@ -197,6 +197,31 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
 }
 
 
+qlin_status qlin_linear_weight_only(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                                    const qlin_segment* segments, int32_t nseg, qlin_out out, hipStream_t stream) {
+    if (out == QLIN_OUT_I32) return QLIN_ERR_UNSUPPORTED;
+    bool noop = false;
+    const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, nullptr, nullptr, true, &noop);
+    if (st != QLIN_OK || noop) return st;
+    if (M > 32) return QLIN_ERR_UNSUPPORTED;
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
+                        : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
+    qlin::SegmentArgs sa{};
+    int n = 0, k = 0;
+    for (int i = 0; i < nseg; ++i) {
+        if (segments[i].n == 0) continue;
+        sa.w[k] = static_cast<const uint8_t*>(segments[i].q_w);
+        sa.sw[k] = segments[i].s_w;
+        sa.y[k] = segments[i].y;
+        sa.start[k] = n;
+        n += (int)segments[i].n;
+        ++k;
+    }
+    sa.nseg = k;
+    for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
+    return hip_status(qlin::launch_weight_only(variant, x, M, K, sa, (int)out, stream));
+}
+
 qlin_status qlin_quant_act_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t stream) {
     bool noop = false;
     const qlin_status st = check_quant(x, M, K, q, s, M, &noop);

@@ -57,6 +57,12 @@ hipError_t launch_linear_decode(int variant, const uint16_t* x, int64_t K, const
                                 uint8_t* qx, float* sx, hipStream_t st);
 constexpr int64_t kDecodeMaxK = 16384;   // fused one-row path keeps the quantized row in LDS/registers
 
+// Weight-only ("equivalent") numerics: bf16 activations times dequantized
+// weights, every segment of sa in one launch.  M <= 32.
+constexpr int64_t kWeightOnlyRowMaxK = 16384;   // one-token kernel keeps the bf16 row in LDS
+hipError_t launch_weight_only(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa, int mode,
+                              hipStream_t st);
+
 int gemv_rows_per_wave(int64_t N, int64_t K);
 int small_waves_per_tile(int64_t N, int64_t K);
 

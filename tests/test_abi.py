@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libqlin.so"
         assert n in Q.SIGNATURES, f"{n} has no binding signature"
@@ -162,6 +162,25 @@ def test_linear_validation():
     assert lin(0, x, 1, 256, nul, 1, 0, None, None, None) == Q.QLIN_ERR_NULL
     empty = (Seg * 1)(Seg(None, None, None, 0))
     assert lin(0, x, 1, 256, empty, 1, 0, None, None, None) == Q.QLIN_OK             # no rows: no-op
+
+
+def test_linear_weight_only_validation():
+    Seg = Q.QlinSegment
+    x = A
+    segs = (Seg * 2)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 128),
+                     Seg(A + 0x4000000, A + 0x5000000, A + 0x6000000, 128))
+    wo = L.qlin_linear_weight_only
+    assert wo(0, x, 1, 256, None, 1, 0, None) == Q.QLIN_ERR_NULL
+    assert wo(0, x, 1, 256, segs, 0, 0, None) == Q.QLIN_ERR_SHAPE
+    assert wo(9, x, 1, 256, segs, 2, 0, None) == Q.QLIN_ERR_UNSUPPORTED
+    assert wo(0, x, 1, 256, segs, 2, Q.OUT_I32, None) == Q.QLIN_ERR_UNSUPPORTED   # no integer accumulator here
+    assert wo(0, x, 33, 256, segs, 2, 0, None) == Q.QLIN_ERR_UNSUPPORTED          # at most 32 tokens
+    assert wo(2, x, 1, 200, segs, 2, 0, None) == Q.QLIN_ERR_SHAPE                 # block: K % 128
+    assert wo(0, x, 0, 256, segs, 2, 0, None) == Q.QLIN_OK                        # M == 0
+    assert wo(0, None, 1, 256, segs, 2, 0, None) == Q.QLIN_ERR_NULL
+    assert wo(0, x + 8, 1, 256, segs, 2, 0, None) == Q.QLIN_ERR_ALIGN
+    bad = (Seg * 1)(Seg(A + 0x1000000, A + 0x2000000, x + 64, 128))             # y overlaps x
+    assert wo(0, x, 4, 256, bad, 1, 0, None) == Q.QLIN_ERR_ALIAS
 
 
 def test_library_has_no_unresolved_internal_symbols():
