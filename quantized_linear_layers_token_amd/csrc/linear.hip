@@ -261,14 +261,15 @@ void launch_kc(int R, int grid, hipStream_t st, const uint16_t* x, int K, const 
 
 }  // namespace
 
-// Launch shape (swept on MI355X over the Llama-3.1-8B decode groups): one
-// group of two rows per wavefront gives the most bytes in flight; rows of up
-// to 8 KiB are read two at a time (R = 2), longer rows one at a time (R = 1,
-// two iterations).  Either way a workgroup covers 8 rows.
+// Launch shape (compared on one MI355X over the Llama-3.1-8B decode step):
+// rows of up to 4 KiB: one row per wavefront (the most workgroups, every load
+// issued at once); up to 8 KiB: two rows per wavefront read together; longer
+// rows: two rows per wavefront read one after the other (R = 1).
 void decode_launch_shape(int64_t ntot, int64_t K, int* R, int* grid) {
     const int64_t kc = (K + 1023) / 1024;
-    *R = (kc <= 8) ? 2 : 1;
-    const int64_t g = (ntot + 7) / 8;
+    *R = (kc > 4 && kc <= 8) ? 2 : 1;
+    const int64_t rows = 4 * (kc <= 4 ? 1 : 2);         // rows per workgroup of four wavefronts
+    const int64_t g = (ntot + rows - 1) / rows;
     *grid = (int)(g < 1 ? 1 : g);
 }
 
