@@ -48,6 +48,7 @@ __all__ = [
     "linear_w8a8", "linear_fp8_rowwise", "linear_fp8_block",
     "epilogue_f32_order",
     "dequantize_weights", "linear_weight_only",
+    "silu", "swiglu_gate_up",
 ]
 
 # Largest code magnitude of each target format.
@@ -376,3 +377,45 @@ def linear_weight_only(x_bits, q_w, s_w_bits, scheme: str):
     w = dequantize_weights(q_w, s_w_bits, scheme)
     y = x @ w.T
     return round_to_bf16_bits(y), y
+
+
+# --------------------------------------------------------------------------
+# SwiGLU on a gate/up pair (the step right after the projections)
+# --------------------------------------------------------------------------
+#
+# The pages stop at the projections; what follows is the plain definition of
+# the gated MLP that the Llama 3.1 and Qwen3 layers (the models of the pages'
+# "Command line" sections) feed into the down projection:
+#     h = silu(x W_gate^T) * (x W_up^T),   silu(t) = t * sigmoid(t) = t / (1 + e^-t).
+# Reading: gate and up are computed as the quantized projections above (one
+# shared rounding of x) and rounded to bf16 like any projection output; silu is
+# applied to that bf16 value and rounded to bf16, and the product with the bf16
+# up value is rounded to bf16 -- the order in which a bf16 model evaluates
+# act(gate) * up.
+
+_LINEAR = {"int8": linear_w8a8, "fp8_rowwise": linear_fp8_rowwise, "fp8_block": linear_fp8_block}
+
+
+def silu(t) -> np.ndarray:
+    """silu(t) = t / (1 + exp(-t)) in fp64.  For t below about -709, exp(-t)
+    overflows to inf and the quotient is -0 (the true value is below 1e-305)."""
+    t = np.asarray(t, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return t / (1.0 + np.exp(-t))
+
+
+def swiglu_gate_up(x_bits, gate, up, scheme: str):
+    """h[m, j] = bf16(bf16(silu(g[m, j])) * u[m, j]) with g, u the bf16 outputs
+    of the gate and up projections of the same input x under `scheme` ("int8",
+    "fp8_rowwise", "fp8_block"); gate and up are (q_w, s_w_bits) pairs of
+    equal shape.
+
+    Returns (h_bits, g_bits, u_bits, g_exact, u_exact): h as bf16 bits [M, I],
+    the two projections' bf16 outputs, and their exact (fp64, unrounded)
+    values."""
+    lin = _LINEAR[scheme]
+    g_bits, g_exact = lin(x_bits, *gate)[:2]
+    u_bits, u_exact = lin(x_bits, *up)[:2]
+    s_bits = round_to_bf16_bits(silu(bf16_bits_to_f64(g_bits)))
+    h_bits = round_to_bf16_bits(bf16_bits_to_f64(s_bits) * bf16_bits_to_f64(u_bits))
+    return h_bits, g_bits, u_bits, g_exact, u_exact

@@ -536,3 +536,65 @@ def test_weight_only_block_reduces_to_rowwise_and_scales_exactly():
     x2 = O.round_to_bf16_bits(O.bf16_bits_to_f64(x) * 4.0)
     _, y4 = O.linear_weight_only(x2, qw, blk, "fp8_block")
     assert np.array_equal(y4, yb * 4.0)
+
+
+# --------------------------------------------------------------------------
+# SwiGLU on a gate/up pair
+# --------------------------------------------------------------------------
+
+def test_silu_closed_forms_and_identities():
+    ln3 = math.log(3.0)
+    # sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(ln3) - 0.75 * ln3) <= 4e-16
+    assert abs(O.silu(-ln3) + 0.25 * ln3) <= 4e-16
+    # silu(t) - silu(-t) = t, and silu(t) = t * sigmoid(t) through scipy's logistic
+    import scipy.special as sp
+    t = np.random.default_rng(7).normal(0.0, 6.0, 4096)
+    assert np.allclose(O.silu(t) - O.silu(-t), t, rtol=0, atol=1e-13 * np.abs(t).max())
+    assert np.allclose(O.silu(t), t * sp.expit(t), rtol=1e-14, atol=1e-300)
+    # limits: large t passes through, very negative t gives (negative) zero
+    assert O.silu(60.0) == 60.0
+    v = O.silu(-800.0)
+    assert v == 0.0 and math.copysign(1.0, v) < 0
+
+
+def _bf16_rne_via_f32(v):
+    """bf16 rounding of fp64 values through float32 and the integer
+    round-half-even trick on the f32 bit pattern (a different route from the
+    oracle's)."""
+    u = np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    return ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("scheme", ["int8", "fp8_rowwise", "fp8_block"])
+def test_swiglu_chain_independent(scheme):
+    """h = bf16(bf16(silu(g)) * u) with g, u the gate and up projections,
+    recomputed with silu in its tanh form, t (1 + tanh(t/2)) / 2."""
+    M, K, I = 3, 256, 256
+    x = W.x_bf16(900, M, K)
+    if scheme == "int8":
+        gate = (W.w_int8(901, I, K), W.scale_bf16(902, I, 1e-4, 5e-4))
+        up = (W.w_int8(903, I, K), W.scale_bf16(904, I, 1e-4, 5e-4))
+        lin = O.linear_w8a8
+    else:
+        shp = (I // 128, K // 128) if scheme == "fp8_block" else (I,)
+        gate = (W.w_e4m3(901, I, K), W.scale_bf16(902, shp, 1e-4, 5e-4))
+        up = (W.w_e4m3(903, I, K), W.scale_bf16(904, shp, 1e-4, 5e-4))
+        lin = O.linear_fp8_rowwise if scheme == "fp8_rowwise" else O.linear_fp8_block
+    h, g_bits, u_bits, g_exact, u_exact = O.swiglu_gate_up(x, gate, up, scheme)
+    # the pair is (gate, up) in that order, each the pinned projection
+    assert np.array_equal(g_bits, lin(x, *gate)[0]) and np.array_equal(u_bits, lin(x, *up)[0])
+    g = O.bf16_bits_to_f64(g_bits)
+    u = O.bf16_bits_to_f64(u_bits)
+    assert (g < -2).any() and (np.abs(g) < 2).any() and (g > 2).any(), "inputs span the curved part of silu"
+    s = O.bf16_bits_to_f64(_bf16_rne_via_f32(g * (1.0 + np.tanh(g / 2.0)) / 2.0))
+    want = _bf16_rne_via_f32(s * u)
+    assert np.array_equal(h, want)
+    # the intermediate rounding matters: a single rounding of silu(g) * u differs somewhere
+    assert not np.array_equal(h, _bf16_rne_via_f32(g * (1.0 + np.tanh(g / 2.0)) / 2.0 * u))
+    # gate and up do not commute
+    h_swapped = O.swiglu_gate_up(x, up, gate, scheme)[0]
+    assert not np.array_equal(h, h_swapped)
+    assert np.allclose(g, g_exact, rtol=2.0 ** -8, atol=0) and np.allclose(u, u_exact, rtol=2.0 ** -8, atol=0)
