@@ -95,6 +95,15 @@ class Launcher:
         self.keep.append(arr)
         self.calls.append((self.L.qlin_linear_weight_only, (scheme, x.data_ptr(), M, K, arr, len(segs), out)))
 
+    def linear_swiglu(self, scheme, x, gate, up, h, qx=None, sx=None):
+        """gate, up: (q_w, s_w) of one MLP; h [M, I] receives silu(gate) * up."""
+        M, K = x.shape
+        self.calls.append((self.L.qlin_linear_swiglu, (scheme, x.data_ptr(), M, K, gate[0].data_ptr(),
+                                                        gate[1].data_ptr(), up[0].data_ptr(), up[1].data_ptr(),
+                                                        gate[0].shape[0], h.data_ptr(),
+                                                        None if qx is None else qx.data_ptr(),
+                                                        None if sx is None else sx.data_ptr())))
+
     def gemm(self, fn, qx, sx, qw, sw, y, M, N, K, out=0, path=0):
         f = getattr(self.L, fn + "_ex")
         self.calls.append((f, (qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
@@ -163,8 +172,12 @@ def build_decode(torch, Q, W, layers, dev):
     """32 layers of int8 projections with distinct weights + per-layer inputs.
     F: the fused step (one qlin_linear launch per layer input: q/k/v, o,
     gate/up, down); L: the two-kernel step (quantizer + one-row product per
-    projection); G: the one-row products alone."""
+    projection); G: the one-row products alone; WO: F under weight-only
+    numerics; S: F with gate/up as one SwiGLU launch whose output h is down's
+    input (returned with its algorithmic bytes)."""
     F = Launcher(Q, torch)
+    S = Launcher(Q, torch)
+    swiglu_step_bytes = 0
     L = Launcher(Q, torch)
     G = Launcher(Q, torch)
     WO = Launcher(Q, torch)
@@ -194,6 +207,20 @@ def build_decode(torch, Q, W, layers, dev):
             F.linear(0, x, [(lw[name][0], lw[name][1], lw[name][2]) for name in group])
             WO.linear_weight_only(0, x, [(lw[name][0], lw[name][1], lw[name][2]) for name in group])
             fused_step_bytes += fused_bytes(K, [shapes[name][0] for name in group])
+            if group == ("gate", "up"):
+                I = shapes["gate"][0]
+                h = torch.empty((1, I), dtype=torch.int16, device=dev)
+                lw["h"] = h
+                S.linear_swiglu(0, x, lw["gate"][:2], lw["up"][:2], h)
+                # bf16 row in, both weights and scales once, h out
+                swiglu_step_bytes += 2 * K + 2 * (I * K + 2 * I) + 2 * I
+            elif group == ("down",):
+                N = shapes["down"][0]
+                S.linear(0, lw["h"], [lw["down"]])
+                swiglu_step_bytes += fused_bytes(K, [N])
+            else:
+                S.linear(0, x, [(lw[name][0], lw[name][1], lw[name][2]) for name in group])
+                swiglu_step_bytes += fused_bytes(K, [shapes[name][0] for name in group])
             for name in group:
                 qw, sw, y = lw[name]
                 N, K2 = shapes[name]
@@ -204,7 +231,7 @@ def build_decode(torch, Q, W, layers, dev):
                 gemv_bytes += b
                 per_shape.setdefault(name, []).append((q, s, qw, sw, y, N, K2))
         bufs.append(lw)
-    return F, L, G, WO, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape
+    return F, L, G, WO, (S, swiglu_step_bytes), bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape
 
 
 def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
@@ -215,6 +242,7 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
     full = Launcher(Q, torch)
     prod = Launcher(Q, torch)
     fused = Launcher(Q, torch)
+    swiglu = Launcher(Q, torch)     # fused, with gate/up as one SwiGLU launch
     scheme = {"int8": Q.SCHEME_W8A8, "fp8_row": Q.SCHEME_FP8_ROWWISE, "fp8_block": Q.SCHEME_FP8_BLOCK}[variant]
     gen = torch.Generator(device=dev)
     ops = 0
@@ -252,7 +280,11 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
                 ops += 2 * M * N * K
             # the group as one call: quantization + one GEMM launch over its segments
             fused.linear(scheme, x, segs, qx=q, sx=s)
-    return full, prod, fused, ops, keep
+            if group == ("gate", "up"):
+                swiglu.linear_swiglu(scheme, x, segs[0][:2], segs[1][:2], segs[0][2], qx=q, sx=s)
+            else:
+                swiglu.linear(scheme, x, segs, qx=q, sx=s)
+    return full, prod, fused, swiglu, ops, keep
 
 
 # ---------------------------------------------------------------------------
@@ -350,7 +382,7 @@ def main():
 
     # ---- headline: decode, M = 1, 32 distinct layers -------------------------
     log("building decode workload (32 layers, int8)")
-    F, L, G, WO, bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape = build_decode(
+    F, L, G, WO, (S, swiglu_step_bytes), bufs, fused_step_bytes, step_bytes, gemv_bytes, per_shape = build_decode(
         torch, Q, W, W.LLAMA_8B_LAYERS, dev)
     torch.cuda.synchronize()
     if args.pmc_workload:
@@ -408,6 +440,13 @@ def main():
     ms_wo = time_events(torch, wo, max(3, args.steps // 2))
     secondary["decode_weight_only"] = {"ms_per_step": round(ms_wo, 4),
                                        "gbs": round(fused_step_bytes / (ms_wo * 1e-3) / 1e9, 1)}
+    # gate/up with SwiGLU in the epilogue, down reading its output
+    sg = capture(torch, S.run, use_graph)
+    sg()
+    ms_sg = time_events(torch, sg, max(3, args.steps // 2))
+    secondary["decode_swiglu_chained"] = {"ms_per_step": round(ms_sg, 4), "launches": len(S.calls),
+                                          "gbs": round(swiglu_step_bytes / (ms_sg * 1e-3) / 1e9, 1)}
+    log(f"swiglu-chained step {ms_sg:.4f} ms {secondary['decode_swiglu_chained']}")
     secondary["decode_two_kernel"] = {
         "ms_per_step": round(ms_two, 4), "gbs": round(step_bytes / (ms_two * 1e-3) / 1e9, 1),
         "gemv_only_gbs": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
@@ -474,17 +513,20 @@ def main():
         for variant, peak in (("int8", MFMA_INT8_PEAK_TOPS), ("fp8_row", MFMA_FP8_PEAK_TOPS),
                               ("fp8_block", MFMA_FP8_PEAK_TOPS)):
             for M in (512, 1024):
-                full, prod, fused, ops, keep = prefill_layer_set(
+                full, prod, fused, swiglu, ops, keep = prefill_layer_set(
                     torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
                 f_full = capture(torch, full.run, use_graph)
                 f_prod = capture(torch, prod.run, use_graph)
                 f_fused = capture(torch, fused.run, use_graph)
+                f_sg = capture(torch, swiglu.run, use_graph)
                 f_full()
                 f_prod()
                 f_fused()
+                f_sg()
                 t_full = time_events(torch, f_full, 5)
                 t_prod = time_events(torch, f_prod, 5)
                 t_fused = time_events(torch, f_fused, 5)
+                t_sg = time_events(torch, f_sg, 5)
                 key = f"prefill_{variant}_M{M}"
                 secondary[key] = {
                     "tops_fused_linear": round(ops / (t_fused * 1e-3) / 1e12, 1),
@@ -493,10 +535,11 @@ def main():
                     "frac_gemm_per_projection": round(ops / (t_prod * 1e-3) / 1e12 / peak, 4),
                     "tops_quant_then_per_projection": round(ops / (t_full * 1e-3) / 1e12, 1),
                     "ms_per_layer_fused": round(t_fused / 4, 4),
+                    "tops_fused_linear_swiglu": round(ops / (t_sg * 1e-3) / 1e12, 1),
                     "shapes": "qwen3-8b" if variant == "fp8_block" else "llama-3.1-8b",
                 }
                 log(f"{key}: {secondary[key]}")
-                del keep, full, prod, fused, f_full, f_prod, f_fused
+                del keep, full, prod, fused, swiglu, f_full, f_prod, f_fused, f_sg
                 torch.cuda.synchronize()
 
     cpu = None

@@ -230,6 +230,29 @@ qlin_status qlin_linear_weight_only(qlin_scheme scheme, const uint16_t* x, int64
                                     const qlin_segment* segments, int32_t nseg, qlin_out out,
                                     hipStream_t stream);
 
+/* Gate/up pair of a gated MLP with SwiGLU applied on the way out.  The pages
+ * stop at the projections; this is the plain definition of the MLP of the
+ * models their "Command line" sections run (Llama 3.1 8B, Qwen3 8B):
+ *   g = x W_gate^T,  u = x W_up^T   -- each exactly as qlin_linear computes it
+ *                                      (one shared rounding of x) and rounded
+ *                                      to bf16 as qlin_linear would write it,
+ *   h[m, j] = bf16( bf16(silu(g[m, j])) * u[m, j] ),  silu(t) = t / (1 + e^-t),
+ * silu evaluated in f32 on the bf16 g.  h is the down projection's input
+ * (qlin_linear rounds it for down in the down projection's own launch).
+ *   gate_q_w, up_q_w: [I, K] codes of the scheme; gate_s_w, up_s_w: bf16 [I]
+ *   (rowwise schemes) or [I/128, K/128] (block scheme; I % 128 == 0);
+ *   h: bf16 [M, I], 16-byte aligned, written.
+ * Same validation, q_x / s_x staging and dispatch as qlin_linear with the two
+ * weights as segments: M == 1 with K <= 16384 is one launch in which each
+ * wavefront streams a gate row and the up row with the same index; otherwise a
+ * quantizer launch, then one product launch whose tiles hold gate rows and the
+ * matching up rows.  Neither g nor u is written to memory.  h may not overlap
+ * x, q_x, s_x or either weight or scale array (QLIN_ERR_ALIAS). */
+qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                               const void* gate_q_w, const uint16_t* gate_s_w,
+                               const void* up_q_w, const uint16_t* up_s_w, int64_t I,
+                               uint16_t* h, void* q_x, float* s_x, hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* Helpers                                                                */
 /* ---------------------------------------------------------------------- */

@@ -41,6 +41,7 @@ SIGNATURES = {
     "qlin_gemm_fp8_block_ex": (_S, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _S, _S, _P]),
     "qlin_linear": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P, _P, _P]),
     "qlin_linear_weight_only": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P]),
+    "qlin_linear_swiglu": (_S, [_S, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P, _P, _P]),
     "qlin_status_string": (ctypes.c_char_p, [_S]),
     "qlin_abi_version": (_S, []),
     "qlin_last_hip_error": (_S, []),
@@ -203,3 +204,16 @@ def qlin_linear_weight_only(scheme, x, segments, out=OUT_BF16, stream=None):
     arr = segments_array(segments)
     _check(_lib.qlin_linear_weight_only(scheme, _ptr(x), M, K, arr, len(segments), out, _stream(stream)),
            "qlin_linear_weight_only")
+
+
+def qlin_linear_swiglu(scheme, x, gate, up, h, q_x=None, s_x=None, stream=None):
+    """x bf16 [M, K]; gate, up: (q_w [I, K], s_w) of one gated MLP; h bf16
+    [M, I] receives silu(gate projection) * (up projection), each rounded as
+    the header states.  q_x / s_x: staging for the quantized activations
+    (optional at M == 1)."""
+    M, K = _dims2(x, "x")
+    (gq, gs), (uq, us) = gate, up
+    if gq.dim() != 2 or gq.shape[1] != K or tuple(uq.shape) != tuple(gq.shape):
+        raise ValueError("gate and up q_w must both be [I, K]")
+    _check(_lib.qlin_linear_swiglu(scheme, _ptr(x), M, K, _ptr(gq), _ptr(gs), _ptr(uq), _ptr(us), gq.shape[0],
+                                   _ptr(h), _ptr(q_x), _ptr(s_x), _stream(stream)), "qlin_linear_swiglu")

@@ -28,6 +28,11 @@
 //
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8; tile ids are
 // assigned so that tiles sharing a weight panel are consecutive on one XCD.
+//
+// SwiGLU mode (SG): the BN weight rows of a tile are BN/2 gate rows j0.. and
+// the up rows with the same indices; the bf16 epilogue tile in LDS then holds
+// gate and up of each (j, m), and the store pass writes
+// h = swiglu_bf16(gate, up), BN/2 columns per tile.
 #include <type_traits>
 
 #include "qlin_device.h"
@@ -46,7 +51,7 @@ template <> struct LargeAcc<VAR_FP8_BLOCK> { typedef v16f T; };
 
 template <int U> using IC = std::integral_constant<int, U>;
 
-template <int V, int BN, int BM, int WN, int WM>
+template <int V, int BN, int BM, int WN, int WM, bool SG>
 __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa,
     int M, int K, int mode, int tiles_m, int tiles_n) {
@@ -77,20 +82,25 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     // results to scalar registers, so the buffer descriptors built from them
     // are scalar (a descriptor the compiler takes as divergent costs a
     // readfirstlane loop around every load).
+    // (SG: a panel is BN/2 gate rows and the same BN/2 up rows)
+    constexpr int PR = SG ? BN / 2 : BN;                   // rows of one segment per panel
     int panel = __builtin_amdgcn_readfirstlane(t / tiles_m), seg = 0;
+    if constexpr (!SG) {
 #pragma unroll
-    for (int i = 0; i + 1 < kMaxSegments; ++i) {
-        const int np = (sa.start[i + 1] - sa.start[i] + BN - 1) / BN;
-        if (seg == i && i + 1 < sa.nseg && panel >= np) {
-            panel -= np;
-            seg = i + 1;
+        for (int i = 0; i + 1 < kMaxSegments; ++i) {
+            const int np = (sa.start[i + 1] - sa.start[i] + BN - 1) / BN;
+            if (seg == i && i + 1 < sa.nseg && panel >= np) {
+                panel -= np;
+                seg = i + 1;
+            }
         }
     }
     const uint8_t* __restrict__ qw = sa.w[seg];
     const uint16_t* __restrict__ sw = sa.sw[seg];
+    const uint16_t* __restrict__ sw_u = sa.sw[SG ? 1 : 0];
     void* __restrict__ y = sa.y[seg];
     const int N = sa.start[seg + 1] - sa.start[seg];
-    const int n0 = panel * BN;
+    const int n0 = panel * PR;
     const int m0 = __builtin_amdgcn_readfirstlane((t % tiles_m) * BM);
 
     // ---- global -> register -> LDS assignment.  Thread tid carries logical
@@ -100,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     constexpr int JW = BN / 32, JX = BM / 32, JR = JW > JX ? JW : JX;
     static_assert(JW + JX == CH, "chunk split");
     const int cthr = tid & 7;
-    const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(BN, N - n0) * K);
+    const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(PR, N - n0) * K);
+    const __amdgpu_buffer_rsrc_t du = uniform_rsrc(sa.w[SG ? 1 : 0] + (int64_t)n0 * K, SG ? min(PR, N - n0) * K : 0);
     const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(qx + (int64_t)m0 * K, min(BM, M - m0) * K);
     int roff[JR];                                          // byte offset of each carried row
 #pragma unroll
@@ -124,7 +135,8 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
         // chunks past K re-read the row's last chunk (zeroed when written to LDS),
         // so every in-range offset stays inside its row
         const int k = min(s * kBK + cthr * 16, K - 16);
-        if (j < JW) r[j] = __builtin_amdgcn_raw_buffer_load_b128(dw, roff[j] + k, 0, 0);
+        if (SG && j >= JW / 2 && j < JW) r[j] = __builtin_amdgcn_raw_buffer_load_b128(du, roff[j - JW / 2] + k, 0, 0);
+        else if (j < JW) r[j] = __builtin_amdgcn_raw_buffer_load_b128(dw, roff[j] + k, 0, 0);
         else r[j] = __builtin_amdgcn_raw_buffer_load_b128(dx, roff[j - JW] + k, 0, 0);
     };
     auto issue_fac = [&](auto set, int s) {
@@ -136,8 +148,11 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
             for (int jj = 0; jj < TM; ++jj)
                 fx[jj] = sx[(int64_t)min(m0 + wm * SM + jj * 32 + (lane & 31), M - 1) * kbs + kb];
 #pragma unroll
-            for (int ii = 0; ii < TN; ++ii)
-                fw[ii] = bf16_lo(sw[(int64_t)(min(n0 + wn * SN + ii * 32, N - 1) >> 7) * kbs + kb]);
+            for (int ii = 0; ii < TN; ++ii) {
+                const int rr = wn * SN + ii * 32;              // tile row (SG: >= BN/2 are up rows)
+                if (SG && rr >= PR) fw[ii] = bf16_lo(sw_u[(int64_t)(min(n0 + rr - PR, N - 1) >> 7) * kbs + kb]);
+                else fw[ii] = bf16_lo(sw[(int64_t)(min(n0 + rr, N - 1) >> 7) * kbs + kb]);
+            }
         }
     };
     auto issue_all = [&](auto set, int s) {
@@ -184,7 +199,8 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
 
     if constexpr (V != VAR_FP8_BLOCK) {
         // the epilogue's scales, staged once
-        for (int i = tid; i < BN; i += kThreads) s_w_t[i] = bf16_lo(sw[min(n0 + i, N - 1)]);
+        for (int i = tid; i < BN; i += kThreads)
+            s_w_t[i] = (SG && i >= PR) ? bf16_lo(sw_u[min(n0 + i - PR, N - 1)]) : bf16_lo(sw[min(n0 + i, N - 1)]);
         for (int i = tid; i < BM; i += kThreads) s_x_t[i] = sx[min(m0 + i, M - 1)];
     }
 
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     // banks), then every thread streams whole 16-byte pieces of output rows,
     // a wave covering 1 KB of contiguous rows per store instead of 32 rows x
     // 16 bytes.
-    if (mode == OUT_BF16 && (N & 7) == 0) {
+    if (SG || (mode == OUT_BF16 && (N & 7) == 0)) {
         constexpr int PITCH = BN * 2 + 16;
         static_assert(BM * PITCH <= (int)sizeof(lds), "bf16 staging tile fits the stage buffers");
         __syncthreads();                                   // every wave is done with the last stage
@@ -351,6 +367,32 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
                 }
         }
         __syncthreads();
+        if constexpr (SG) {
+            // gate of (row, j) at column j - n0, up at column PR + j - n0
+            constexpr int CPH = PR * 2 / 16;               // 16-byte pieces per h row
+            for (int id = tid; id < BM * CPH; id += kThreads) {
+                const int row = id / CPH, c = id % CPH;
+                const int m = m0 + row, j = n0 + 8 * c;
+                if (m >= M || j >= N) continue;
+                const v4u g = *reinterpret_cast<const v4u*>(lds + row * PITCH + 16 * c);
+                const v4u u = *reinterpret_cast<const v4u*>(lds + row * PITCH + PR * 2 + 16 * c);
+                const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
+                uint32_t hw[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    hw[q] = (uint32_t)swiglu_bf16(bf16_lo(gw[q]), bf16_lo(uw[q])) |
+                            ((uint32_t)swiglu_bf16(bf16_hi(gw[q]), bf16_hi(uw[q])) << 16);
+                uint16_t* hp = static_cast<uint16_t*>(y) + (int64_t)m * N + j;
+                if ((N & 7) == 0) {
+                    *reinterpret_cast<v4u*>(hp) = v4u{hw[0], hw[1], hw[2], hw[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (j + e < N) hp[e] = (uint16_t)(hw[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+            return;
+        }
         constexpr int CPR = BN * 2 / 16;                   // 16-byte pieces per tile row
 #pragma unroll 4
         for (int id = tid; id < BM * CPR; id += kThreads) {
@@ -410,11 +452,17 @@ template <int V, int BN, int BM, int WN, int WM>
 hipError_t launch_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K, int mode,
                        hipStream_t st) {
     const int tm = (int)((M + BM - 1) / BM);
+    dim3 block(kThreads);
+    if (mode == OUT_SWIGLU) {
+        const int tn = (sa.start[1] + BN / 2 - 1) / (BN / 2);
+        hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, true>), dim3((unsigned)(tm * tn)), block, 0, st, qx,
+                           sx, sa, (int)M, (int)K, mode, tm, tn);
+        return hipGetLastError();
+    }
     int tn = 0;
     for (int i = 0; i < sa.nseg; ++i) tn += (sa.start[i + 1] - sa.start[i] + BN - 1) / BN;
-    dim3 grid((unsigned)(tm * tn)), block(kThreads);
-    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM>), grid, block, 0, st, qx, sx, sa, (int)M, (int)K, mode,
-                       tm, tn);
+    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, false>), dim3((unsigned)(tm * tn)), block, 0, st, qx, sx,
+                       sa, (int)M, (int)K, mode, tm, tn);
     return hipGetLastError();
 }
 

@@ -23,6 +23,10 @@
 //               weight scales, per-128-input activation scales).
 //   split-K   = the NW partial tiles are summed through LDS, then the scale
 //               epilogue writes y.
+//   SwiGLU    = (SG) the first RT/2 MFMA row tiles are gate rows j0.., the
+//               other RT/2 the up rows with the same indices: after the
+//               reduction a lane holds gate and up of the same (j, m) and
+//               writes h = swiglu_bf16(gate, up).
 #include <type_traits>
 
 #include "qlin_device.h"
@@ -41,7 +45,7 @@ template <int V> struct SmallAcc { typedef v4i T; };
 template <> struct SmallAcc<VAR_FP8_ROW> { typedef v4f T; };
 template <> struct SmallAcc<VAR_FP8_BLOCK> { typedef v4f T; };
 
-template <int V, int MT, int NW, int RT>
+template <int V, int MT, int NW, int RT, bool SG>
 __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode) {
     typedef typename SmallAcc<V>::T Acc;
@@ -55,14 +59,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
 
     // tiles of 16 RT weight rows (RT MFMA tiles sharing the token loads) are numbered across the segments (q, k, v or gate, up
     // sharing one input); a tile never straddles two segments
-    constexpr int TR = 16 * RT;
+    // (SG: a tile is 8 RT gate rows and the same 8 RT up rows)
+    static_assert(!SG || RT % 2 == 0, "SwiGLU tiles pair gate and up row tiles");
+    constexpr int TR = SG ? 8 * RT : 16 * RT;          // rows of one segment per tile
+    constexpr int RH = SG ? RT / 2 : RT;               // row tiles per segment
     int tile = blockIdx.x, seg = 0;
+    if constexpr (!SG) {
 #pragma unroll
-    for (int i = 0; i + 1 < kMaxSegments; ++i) {
-        const int nt = (sa.start[i + 1] - sa.start[i] + TR - 1) / TR;
-        if (seg == i && i + 1 < sa.nseg && tile >= nt) {
-            tile -= nt;
-            seg = i + 1;
+        for (int i = 0; i + 1 < kMaxSegments; ++i) {
+            const int nt = (sa.start[i + 1] - sa.start[i] + TR - 1) / TR;
+            if (seg == i && i + 1 < sa.nseg && tile >= nt) {
+                tile -= nt;
+                seg = i + 1;
+            }
         }
     }
     const uint8_t* __restrict__ qw = sa.w[seg];
@@ -80,6 +89,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     // rows: rows past N or M, K past the end and steps past the wave's range
     // read as zero (an out-of-range offset), with no select after the load.
     const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(TR, N - n0) * K);
+    // SG: the up rows with the same indices (segment 1, equal width)
+    const __amdgpu_buffer_rsrc_t du = uniform_rsrc(sa.w[SG ? 1 : 0] + (int64_t)n0 * K, SG ? min(TR, N - n0) * K : 0);
     const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(qx, M * K);
     // Lane (r16, grp) takes bytes [16 grp, 16 grp + 16) and [64 + 16 grp, ...)
     // of each 128-byte step, so one load instruction covers one contiguous
@@ -93,6 +104,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
 
     const int kbs = K >> 7;
     const uint16_t* swblk = sw + (int64_t)(n0 >> 7) * kbs;  // block FP8: the tile's 128-row block
+    const uint16_t* swblk_u = sa.sw[SG ? 1 : 0] + (int64_t)(n0 >> 7) * kbs;
 
     Acc acc[RT][MT];
 #pragma unroll
@@ -105,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     // in flight.  Loads past the wavefront's steps read zero.
     constexpr int U = RT == 1 ? 2 * kSmallBatch : kSmallBatch;   // same register budget either way
     v4u wa[2][U][RT][2], xa[2][U][MT][2];
-    float fx[2][U][MT], fw[2][U];
+    float fx[2][U][MT], fw[2][U][SG ? 2 : 1];
     auto issue = [&](auto bufc, int s0) {
         constexpr int bi = decltype(bufc)::value;
 #pragma unroll
@@ -117,9 +129,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
             // weights stream once: non-temporal
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const int o = woff + r * 16 * K + s * 128;
-                wa[bi][u][r][0] = __builtin_amdgcn_raw_buffer_load_b128(dw, ok0 ? o : kOOB, 0, kAuxStream);
-                wa[bi][u][r][1] = __builtin_amdgcn_raw_buffer_load_b128(dw, ok1 ? o + 64 : kOOB, 0, kAuxStream);
+                const bool up = SG && r >= RH;
+                const int o = woff + (up ? r - RH : r) * 16 * K + s * 128;
+                wa[bi][u][r][0] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok0 ? o : kOOB, 0, kAuxStream);
+                wa[bi][u][r][1] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok1 ? o + 64 : kOOB, 0, kAuxStream);
             }
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
@@ -128,7 +141,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
             }
             if constexpr (V == VAR_FP8_BLOCK) {
                 const int sb = min(s, s_end - 1);
-                fw[bi][u] = bf16_lo(swblk[sb]);
+                fw[bi][u][0] = bf16_lo(swblk[sb]);
+                if constexpr (SG) fw[bi][u][1] = bf16_lo(swblk_u[sb]);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) fx[bi][u][t] = sx[(int64_t)min(t * 16 + r16, M - 1) * kbs + sb];
             }
@@ -157,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                             const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                             if (s0 + u < s_end) {
-                                const float f = fx[bi][u][t] * fw[bi][u];
+                                const float f = fx[bi][u][t] * fw[bi][u][(SG && r >= RH) ? 1 : 0];
                                 acc[r][t].x = __builtin_fmaf(p.x, f, acc[r][t].x);
                                 acc[r][t].y = __builtin_fmaf(p.y, f, acc[r][t].y);
                                 acc[r][t].z = __builtin_fmaf(p.z, f, acc[r][t].z);
@@ -189,6 +203,41 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
 
     // Sum the NW partial tiles.  Item (r, t, l): weight rows n0 + 16 r + 4 (l / 16)
     // .. + 3 of token m = 16 t + l % 16.
+    if constexpr (SG) {
+        for (int it = tid; it < RH * MT * kWave; it += NW * kWave) {
+            const int rt = it / kWave, l = it % kWave;
+            const int r = rt / MT, t = rt % MT;
+            const int ru = (r + RH) * MT + t;
+            Acc g = red[0][rt][l], u = red[0][ru][l];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                g += red[w][rt][l];
+                u += red[w][ru][l];
+            }
+            const int m = t * 16 + (l & 15);
+            if (m < M) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = n0 + 16 * r + (l >> 4) * 4 + e;
+                    if (n < N) {
+                        float gv, uv;
+                        if constexpr (V == VAR_INT8) {
+                            gv = (float)g[e] * (sx[m] * bf16_lo(sw[n]));
+                            uv = (float)u[e] * (sx[m] * bf16_lo(sa.sw[1][n]));
+                        } else if constexpr (V == VAR_FP8_ROW) {
+                            gv = g[e] * (sx[m] * bf16_lo(sw[n]));
+                            uv = u[e] * (sx[m] * bf16_lo(sa.sw[1][n]));
+                        } else {
+                            gv = g[e];
+                            uv = u[e];
+                        }
+                        static_cast<uint16_t*>(y)[(int64_t)m * N + n] = swiglu_bf16(gv, uv);
+                    }
+                }
+            }
+        }
+        return;
+    }
     for (int it = tid; it < RT * MT * kWave; it += NW * kWave) {
         const int rt = it / kWave, l = it % kWave;
         const int r = rt / MT, t = rt % MT;
@@ -211,13 +260,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     }
 }
 
-template <int V, int MT, int RT>
+template <int V, int MT, int RT, bool SG = false>
 void launch_mt(int nw, dim3 grid, hipStream_t st, const uint8_t* qx, const float* sx, const SegmentArgs& sa,
                int M, int K, int mode) {
     if (nw >= 8)
-        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 8, RT>), grid, dim3(8 * 64), 0, st, qx, sx, sa, M, K, mode);
+        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 8, RT, SG>), grid, dim3(8 * 64), 0, st, qx, sx, sa, M, K, mode);
     else
-        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 4, RT>), grid, dim3(4 * 64), 0, st, qx, sx, sa, M, K, mode);
+        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 4, RT, SG>), grid, dim3(4 * 64), 0, st, qx, sx, sa, M, K, mode);
 }
 
 int64_t small_tiles(const SegmentArgs& sa, int rows) {
@@ -237,6 +286,31 @@ int small_waves_per_tile(int64_t N, int64_t K) {
 
 hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
                              int64_t K, int mode, hipStream_t st) {
+    if (mode == OUT_SWIGLU) {
+        // tiles of 32 gate + 32 up rows with a workgroup per CU or more, else 16 + 16
+        const int64_t I = sa.start[1];
+        const bool wide = (I + 31) / 32 >= 256;
+        const int64_t tiles = (I + (wide ? 31 : 15)) / (wide ? 32 : 16);
+        dim3 grid((unsigned)tiles);
+        const int nw = small_waves_per_tile(tiles, K);
+        const int m = (int)M, k = (int)K;
+        const bool two = M > 16;
+#define QLIN_SMALL_SG(VV)                                                                   \
+        do {                                                                                \
+            if (wide) {                                                                     \
+                if (two) launch_mt<VV, 2, 4, true>(nw, grid, st, qx, sx, sa, m, k, mode);   \
+                else launch_mt<VV, 1, 4, true>(nw, grid, st, qx, sx, sa, m, k, mode);       \
+            } else {                                                                        \
+                if (two) launch_mt<VV, 2, 2, true>(nw, grid, st, qx, sx, sa, m, k, mode);   \
+                else launch_mt<VV, 1, 2, true>(nw, grid, st, qx, sx, sa, m, k, mode);       \
+            }                                                                               \
+        } while (0)
+        if (variant == VAR_INT8) QLIN_SMALL_SG(VAR_INT8);
+        else if (variant == VAR_FP8_ROW) QLIN_SMALL_SG(VAR_FP8_ROW);
+        else QLIN_SMALL_SG(VAR_FP8_BLOCK);
+#undef QLIN_SMALL_SG
+        return hipGetLastError();
+    }
     // 64-row tiles share each token load four ways, but only pay off with at
     // least a workgroup per CU for every 64 rows (the wide gate/up launch)
     const bool wide = small_tiles(sa, 64) >= 256;

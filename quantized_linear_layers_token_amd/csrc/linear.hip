@@ -15,6 +15,11 @@
 // concatenated rows of all segments are split evenly over the wavefronts of the
 // grid; each wavefront reads R rows at a time with 16-byte non-temporal loads
 // (one wave instruction = 1 KiB of one row) and reduces with DPP.
+//
+// SwiGLU mode (SG): segments 0 and 1 are the gate and up weights of one MLP;
+// the work items are the intermediate indices j, a wavefront reads gate row j
+// and up row j together and writes h[j] = swiglu_bf16(gate_j, up_j), the bf16
+// input of the down projection.
 #include "qlin_device.h"
 #include "qlin_internal.h"
 
@@ -87,14 +92,16 @@ __device__ __forceinline__ float dot16_e4m3(const v4u& w, const v4u& x) {
     return a + b;
 }
 
-// V: scheme; KC: 1 KiB slices per row in registers (K <= 1024 KC); R: rows per
-// wave per iteration.  CPT = bf16 chunks of 8 per thread for the rounding.
-template <int V, int KC, int R>
+// V: scheme; KC: 1 KiB slices per row in registers (K <= 1024 KC); R: rows
+// (SG: gate/up row pairs) per wave per iteration; SG: SwiGLU mode.  CPT = bf16
+// chunks of 8 per thread for the rounding.
+template <int V, int KC, int R, bool SG>
 __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     const uint16_t* __restrict__ x, int K, SegmentArgs sa, int mode,
     uint8_t* __restrict__ qx_out, float* __restrict__ sx_out) {
     constexpr bool FP8 = V != VAR_INT8;
     constexpr int CPT = (KC + 1) / 2;
+    constexpr int RL = SG ? 2 * R : R;   // weight rows loaded per iteration
     __shared__ uint32_t red[kThreads / kWave];
     __shared__ __attribute__((aligned(16))) uint8_t xq[KC * 1024];
     __shared__ float gsc[KC * 8];   // block scheme: one scale per 128-input group
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
 #pragma unroll
     for (int j = 0; j < CPT; ++j) xb[j] = xv[min(tid + j * kThreads, nchunks - 1)];
 
-    const int ntot = sa.start[sa.nseg];
+    const int ntot = SG ? sa.start[1] : sa.start[sa.nseg];   // work items: rows, or gate/up pairs
     const int W = gridDim.x * (kThreads / kWave);
     const int w = blockIdx.x * (kThreads / kWave) + wave;
     const int rb = (int)((int64_t)ntot * w / W);
@@ -127,17 +134,29 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         for (int t = 1; t < kMaxSegments; ++t) i += (t < sa.nseg && r >= sa.start[t]) ? 1 : 0;
         return i;
     };
-    auto load_rows = [&](v4u (&dst)[R][KC], int n0) {
+    // loaded row r of the group at work item n0: its segment and row within it
+    // (items past the wave's range re-read a valid row)
+    auto row_of = [&](int r, int n0, int& i, int& local) {
+        if constexpr (SG) {
+            local = max(min(n0 + r / 2, re - 1), 0);
+            i = r & 1;
+        } else {
+            const int n = max(min(n0 + r, re - 1), 0);
+            i = seg_of(n);
+            local = n - sa.start[i];
+        }
+    };
+    auto load_rows = [&](v4u (&dst)[RL][KC], int n0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int n = max(min(n0 + r, re - 1), 0);   // rows past the wave's range re-read a valid row
-            const int i = seg_of(n);
-            const v4u* wrow = reinterpret_cast<const v4u*>(sa.w[i] + (int64_t)(n - sa.start[i]) * K);
+        for (int r = 0; r < RL; ++r) {
+            int i, local;
+            row_of(r, n0, i, local);
+            const v4u* wrow = reinterpret_cast<const v4u*>(sa.w[i] + (int64_t)local * K);
 #pragma unroll
             for (int j = 0; j < KC; ++j) dst[r][j] = __builtin_nontemporal_load(wrow + min(j * kWave + lane, k16 - 1));
         }
     };
-    v4u cur[R][KC];
+    v4u cur[RL][KC];
     load_rows(cur, rb);     // unconditional: the rounding below only waits for the bf16 row
 
     // ---- activation rounding into LDS
@@ -197,11 +216,11 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     const int kbs = K >> 7;
 
     // ---- stream the weight rows: the first group was loaded before the rounding
-    auto process = [&](const v4u (&wr)[R][KC], int n0) {
-        float facc[R];
-        int iacc[R];
+    auto process = [&](const v4u (&wr)[RL][KC], int n0) {
+        float facc[RL];
+        int iacc[RL];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < RL; ++r) {
             if constexpr (V == VAR_INT8) {
                 int a = 0;
 #pragma unroll
@@ -213,9 +232,9 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
                 for (int j = 0; j < KC; ++j) a += dot16_e4m3(wr[r][j], xr[j]);
                 facc[r] = wave_sum_f32(a);
             } else {
-                const int n = max(min(n0 + r, re - 1), 0);
-                const int i = seg_of(n);
-                const uint16_t* swr = sa.sw[i] + (int64_t)((n - sa.start[i]) >> 7) * kbs;
+                int i, local;
+                row_of(r, n0, i, local);
+                const uint16_t* swr = sa.sw[i] + (int64_t)(local >> 7) * kbs;
                 float a = 0.0f;
 #pragma unroll
                 for (int j = 0; j < KC; ++j) {
@@ -224,6 +243,28 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
                 }
                 facc[r] = wave_sum_f32(a);
             }
+        }
+        if constexpr (SG) {
+            if (lane < R && n0 + lane < re) {
+                const int j = n0 + lane;
+                float g = 0.0f, u = 0.0f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (lane != r) continue;
+                    if constexpr (V == VAR_INT8) {
+                        g = (float)iacc[2 * r] * (s_tok * bf16_lo(sa.sw[0][j]));
+                        u = (float)iacc[2 * r + 1] * (s_tok * bf16_lo(sa.sw[1][j]));
+                    } else if constexpr (V == VAR_FP8_ROW) {
+                        g = facc[2 * r] * (s_tok * bf16_lo(sa.sw[0][j]));
+                        u = facc[2 * r + 1] * (s_tok * bf16_lo(sa.sw[1][j]));
+                    } else {
+                        g = facc[2 * r];
+                        u = facc[2 * r + 1];
+                    }
+                }
+                static_cast<uint16_t*>(sa.y[0])[j] = swiglu_bf16(g, u);
+            }
+            return;
         }
         if (lane < R && n0 + lane < re) {
             const int n = n0 + lane;
@@ -253,10 +294,19 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
 template <int V, int KC>
 void launch_kc(int R, int grid, hipStream_t st, const uint16_t* x, int K, const SegmentArgs& sa, int mode,
                uint8_t* qx, float* sx) {
-    if (R >= 2)
-        hipLaunchKernelGGL((linear_decode_kernel<V, KC, 2>), dim3(grid), dim3(kThreads), 0, st, x, K, sa, mode, qx, sx);
-    else
-        hipLaunchKernelGGL((linear_decode_kernel<V, KC, 1>), dim3(grid), dim3(kThreads), 0, st, x, K, sa, mode, qx, sx);
+    if (mode == OUT_SWIGLU)
+        hipLaunchKernelGGL((linear_decode_kernel<V, KC, 1, true>), dim3(grid), dim3(kThreads), 0, st, x, K, sa, mode,
+                           qx, sx);
+    else if constexpr (KC > 4 && KC <= 8) {   // the only row lengths read two rows at a time
+        if (R >= 2)
+            hipLaunchKernelGGL((linear_decode_kernel<V, KC, 2, false>), dim3(grid), dim3(kThreads), 0, st, x, K, sa,
+                               mode, qx, sx);
+        else
+            hipLaunchKernelGGL((linear_decode_kernel<V, KC, 1, false>), dim3(grid), dim3(kThreads), 0, st, x, K, sa,
+                               mode, qx, sx);
+    } else
+        hipLaunchKernelGGL((linear_decode_kernel<V, KC, 1, false>), dim3(grid), dim3(kThreads), 0, st, x, K, sa, mode,
+                           qx, sx);
 }
 
 }  // namespace
@@ -265,6 +315,8 @@ void launch_kc(int R, int grid, hipStream_t st, const uint16_t* x, int K, const 
 // rows of up to 4 KiB: one row per wavefront (the most workgroups, every load
 // issued at once); up to 8 KiB: two rows per wavefront read together; longer
 // rows: two rows per wavefront read one after the other (R = 1).
+// SwiGLU mode: a wavefront reads one gate/up row pair at a time (two rows in
+// flight), one pair per wavefront for rows up to 4 KiB, else two in turn.
 void decode_launch_shape(int64_t ntot, int64_t K, int* R, int* grid) {
     const int64_t kc = (K + 1023) / 1024;
     *R = (kc > 4 && kc <= 8) ? 2 : 1;
@@ -275,7 +327,7 @@ void decode_launch_shape(int64_t ntot, int64_t K, int* R, int* grid) {
 
 hipError_t launch_linear_decode(int variant, const uint16_t* x, int64_t K, const SegmentArgs& sa, int mode,
                                 uint8_t* qx, float* sx, hipStream_t st) {
-    const int64_t ntot = sa.start[sa.nseg];
+    const int64_t ntot = mode == OUT_SWIGLU ? sa.start[1] : sa.start[sa.nseg];
     int R, grid;
     decode_launch_shape(ntot, K, &R, &grid);
     const int64_t kc = (K + 1023) / 1024;

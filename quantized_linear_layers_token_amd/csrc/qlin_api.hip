@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/qlin.h"
+#include "qlin_device.h"
 #include "qlin_internal.h"
 
 namespace {
@@ -220,6 +221,45 @@ qlin_status qlin_linear_weight_only(qlin_scheme scheme, const uint16_t* x, int64
     sa.nseg = k;
     for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
     return hip_status(qlin::launch_weight_only(variant, x, M, K, sa, (int)out, stream));
+}
+
+qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const void* gate_q_w,
+                               const uint16_t* gate_s_w, const void* up_q_w, const uint16_t* up_s_w, int64_t I,
+                               uint16_t* h, void* q_x, float* s_x, hipStream_t stream) {
+    const bool fused = (M == 1) && (K <= qlin::kDecodeMaxK);
+    // the gate and up projections each checked as a bf16 projection into h:
+    // together this covers h against x, the staging buffers and both weights
+    const qlin_segment gate{gate_q_w, gate_s_w, h, I}, up{up_q_w, up_s_w, h, I};
+    bool noop = false;
+    qlin_status st = check_linear(scheme, x, M, K, &gate, 1, QLIN_OUT_BF16, q_x, s_x, fused, &noop);
+    if (st != QLIN_OK || noop) return st;
+    st = check_linear(scheme, x, M, K, &up, 1, QLIN_OUT_BF16, q_x, s_x, fused, &noop);
+    if (st != QLIN_OK || noop) return st;
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
+                        : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
+    qlin::SegmentArgs sa{};
+    sa.w[0] = static_cast<const uint8_t*>(gate_q_w);
+    sa.w[1] = static_cast<const uint8_t*>(up_q_w);
+    sa.sw[0] = gate_s_w;
+    sa.sw[1] = up_s_w;
+    sa.y[0] = sa.y[1] = h;
+    sa.start[0] = 0;
+    sa.start[1] = (int)I;
+    for (int i = 2; i <= qlin::kMaxSegments; ++i) sa.start[i] = (int)(2 * I);
+    sa.nseg = 2;
+    const int mode = qlin::OUT_SWIGLU;
+    if (fused)
+        return hip_status(qlin::launch_linear_decode(variant, x, K, sa, mode, static_cast<uint8_t*>(q_x), s_x, stream));
+    hipError_t e;
+    if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);
+    else e = qlin::launch_quant_fp8(x, M, K, variant == qlin::VAR_FP8_BLOCK ? 128 : 0, static_cast<uint8_t*>(q_x),
+                                    s_x, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (M > 32)
+        return hip_status(qlin::launch_gemm_large(variant, static_cast<const uint8_t*>(q_x), s_x, sa, M, K, mode,
+                                                  stream));
+    return hip_status(qlin::launch_gemm_small(variant, static_cast<const uint8_t*>(q_x), s_x, sa, M, K, mode,
+                                              stream));
 }
 
 qlin_status qlin_quant_act_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t stream) {

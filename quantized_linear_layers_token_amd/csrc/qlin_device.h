@@ -15,7 +15,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-enum OutMode : int { OUT_BF16 = 0, OUT_I32 = 1, OUT_F32 = 2 };
+enum OutMode : int { OUT_BF16 = 0, OUT_I32 = 1, OUT_F32 = 2,
+                     // gate/up pair: segments 0 and 1 are the gate and up weights (equal
+                     // widths), y[0] receives bf16 silu(gate) * up (swiglu_bf16)
+                     OUT_SWIGLU = 3 };
 
 // A raw buffer descriptor over [base, base + bytes): loads at offsets at or
 // past `bytes` return zero.  Arguments must be wave-uniform; they are moved to
@@ -170,6 +173,18 @@ __device__ __forceinline__ void store4_f32(void* y, int64_t idx, const float (&v
         const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
         *reinterpret_cast<v2u*>(static_cast<uint16_t*>(y) + idx) = v2u{lo, hi};
     }
+}
+
+// SwiGLU of one gate/up output pair.  Each projection output is first rounded
+// to bf16, as the projection alone would write it; silu(t) = t / (1 + e^-t) is
+// evaluated in f32 on that value and rounded to bf16, and the product with the
+// bf16 up value is rounded to bf16.  (For t below about -88, e^-t is +inf in
+// f32 and the quotient is -0; the true value is then below 1e-36.)
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
+    const float gb = bf16_lo(f32_to_bf16(g));
+    const float ub = bf16_lo(f32_to_bf16(u));
+    const float s = bf16_lo(f32_to_bf16(gb / (1.0f + __expf(-gb))));
+    return f32_to_bf16(s * ub);
 }
 
 // E4M3 pair decode (bytes 0/1 when HI == false, bytes 2/3 when HI == true).

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libqlin.so"
         assert n in Q.SIGNATURES, f"{n} has no binding signature"
@@ -181,6 +181,26 @@ def test_linear_weight_only_validation():
     assert wo(0, x + 8, 1, 256, segs, 2, 0, None) == Q.QLIN_ERR_ALIGN
     bad = (Seg * 1)(Seg(A + 0x1000000, A + 0x2000000, x + 64, 128))             # y overlaps x
     assert wo(0, x, 4, 256, bad, 1, 0, None) == Q.QLIN_ERR_ALIAS
+
+
+def test_linear_swiglu_validation():
+    sg = L.qlin_linear_swiglu
+    x, gq, gs, uq, us, h = A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x5000000
+    qx, sx = A + 0x6000000, A + 0x7000000
+    assert sg(9, x, 1, 256, gq, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_UNSUPPORTED
+    assert sg(0, x, 0, 256, gq, gs, uq, us, 128, h, None, None, None) == Q.QLIN_OK       # M == 0
+    assert sg(0, x, 1, 256, gq, gs, uq, us, 0, h, None, None, None) == Q.QLIN_OK         # I == 0
+    assert sg(0, x, 1, 250, gq, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_SHAPE
+    assert sg(2, x, 1, 256, gq, gs, uq, us, 64, h, None, None, None) == Q.QLIN_ERR_SHAPE  # block: I % 128
+    assert sg(0, x, 1, 256, None, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL
+    assert sg(0, x, 1, 256, gq, gs, None, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL
+    assert sg(0, x, 1, 256, gq, gs, uq, us, 128, None, None, None, None) == Q.QLIN_ERR_NULL
+    assert sg(0, x, 4, 256, gq, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL  # M > 1 needs staging
+    assert sg(0, x, 1, 256, gq, gs, uq, us, 128, h + 8, None, None, None) == Q.QLIN_ERR_ALIGN
+    assert sg(0, x, 1, 256, gq, gs, uq + 8, us, 128, h, None, None, None) == Q.QLIN_ERR_ALIGN
+    assert sg(0, x, 1, 256, gq, gs, uq, us, 128, uq + 256, None, None, None) == Q.QLIN_ERR_ALIAS  # h in up
+    assert sg(0, x, 1, 256, gq, gs, uq, us, 128, gs, None, None, None) == Q.QLIN_ERR_ALIAS        # h on gate scales
+    assert sg(0, x, 4, 256, gq, gs, uq, us, 128, qx, qx, sx, None) == Q.QLIN_ERR_ALIAS            # h on staging
 
 
 def test_library_has_no_unresolved_internal_symbols():
