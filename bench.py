@@ -287,6 +287,50 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
     return full, prod, fused, swiglu, ops, keep
 
 
+def layer_set(torch, Q, W, scheme, shapes, M, layers, dev, seed0):
+    """`layers` layers of one projection set with distinct weights, one
+    qlin_linear call per layer input (quantization + product; at M = 1 one
+    launch).  Returns (launcher, algorithmic bytes, ops, buffers): bytes are
+    the bf16 inputs, every weight byte and scale once and the bf16 outputs."""
+    shp = dict((n, (N, K)) for n, N, K in shapes)
+    block = scheme == Q.SCHEME_FP8_BLOCK
+    Lr = Launcher(Q, torch)
+    gen = torch.Generator(device=dev)
+    nbytes = ops = 0
+    keep = []
+    for layer in range(layers):
+        gen.manual_seed(seed0 + layer)
+        for group in W.INPUT_GROUPS:
+            K = shp[group[0]][1]
+            x = W.torch_x_bf16(torch, gen, M, K, dev)
+            qx = sx = None
+            if M > 1:
+                qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                sx = torch.empty((M, K // 128) if block else (M,), dtype=torch.float32, device=dev)
+            segs = []
+            nbytes += 2 * M * K
+            for name in group:
+                N = shp[name][0]
+                if scheme == Q.SCHEME_W8A8:
+                    qw = W.torch_w_int8(torch, gen, N, K, dev)
+                else:
+                    qw = W.torch_w_e4m3(torch, gen, N, K, dev)
+                sw = W.torch_scale_bf16(torch, gen, (N // 128, K // 128) if block else (N,), dev)
+                y = torch.empty((M, N), dtype=torch.int16, device=dev)
+                segs.append((qw, sw, y))
+                nbytes += N * K + 2 * sw.numel() + 2 * M * N
+                ops += 2 * M * N * K
+            keep += [x, qx, sx, segs]
+            Lr.linear(scheme, x, segs, qx=qx, sx=sx)
+    return Lr, nbytes, ops, keep
+
+
+def time_launcher(torch, Lr, use_graph, reps=10):
+    fn = capture(torch, Lr.run, use_graph)
+    fn()
+    return time_events(torch, fn, reps)
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle leg
 # ---------------------------------------------------------------------------
@@ -466,6 +510,47 @@ def main():
         secondary["decode_gemv_gbs_per_shape"] = shape_gbs
         log(f"per-shape GB/s {shape_gbs}")
 
+        # the five workloads' other configurations, each with qlin_linear
+        # (quantization included) over distinct weights larger than the MALL
+        cfgs = {}
+        # one W8A8 projection M = 16, N = K = 4096 (32 weight copies rotated)
+        c1 = Launcher(Q, torch)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        keep = []
+        for _ in range(32):
+            x = W.torch_x_bf16(torch, gen, 16, 4096, dev)
+            qw = W.torch_w_int8(torch, gen, 4096, 4096, dev)
+            sw = W.torch_scale_bf16(torch, gen, (4096,), dev)
+            y = torch.empty((16, 4096), dtype=torch.int16, device=dev)
+            qx = torch.empty((16, 4096), dtype=torch.uint8, device=dev)
+            sx = torch.empty((16,), dtype=torch.float32, device=dev)
+            keep.append((x, qw, sw, y, qx, sx))
+            c1.linear(Q.SCHEME_W8A8, x, [(qw, sw, y)], qx=qx, sx=sx)
+        t = time_launcher(torch, c1, use_graph) / 32
+        b1 = 2 * 16 * 4096 + 4096 * 4096 + 2 * 4096 + 2 * 16 * 4096
+        cfgs["w8a8_M16_N4096_K4096"] = {"us_per_call": round(t * 1e3, 3), "gbs": round(b1 / (t * 1e-3) / 1e9, 1),
+                                        "tops": round(2 * 16 * 4096 * 4096 / (t * 1e-3) / 1e12, 2)}
+        del keep, c1
+        for label, scheme, shapes, M, layers, seed in (
+                ("w8a8_llama_M4", Q.SCHEME_W8A8, W.LLAMA_8B, 4, 4, 204),
+                ("w8a8_llama_M8", Q.SCHEME_W8A8, W.LLAMA_8B, 8, 4, 208),
+                ("w8a8_llama_M16", Q.SCHEME_W8A8, W.LLAMA_8B, 16, 4, 216),
+                ("w8a8_llama_M32", Q.SCHEME_W8A8, W.LLAMA_8B, 32, 4, 232),
+                ("fp8_rowwise_llama_M1", Q.SCHEME_FP8_ROWWISE, W.LLAMA_8B, 1, W.LLAMA_8B_LAYERS, 401),
+                ("fp8_rowwise_llama_M32", Q.SCHEME_FP8_ROWWISE, W.LLAMA_8B, 32, 4, 432),
+                ("fp8_block_qwen3_M1", Q.SCHEME_FP8_BLOCK, W.QWEN3_8B, 1, W.QWEN3_8B_LAYERS, 501),
+                ("fp8_block_qwen3_M32", Q.SCHEME_FP8_BLOCK, W.QWEN3_8B, 32, 4, 532)):
+            Lr, nbytes, ops, keep = layer_set(torch, Q, W, scheme, shapes, M, layers, dev, seed)
+            t = time_launcher(torch, Lr, use_graph)
+            cfgs[label] = {"ms_per_pass": round(t, 4), "layers": layers, "launches": len(Lr.calls),
+                           "gbs": round(nbytes / (t * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "tops": round(ops / (t * 1e-3) / 1e12, 2)}
+            log(f"{label}: {cfgs[label]}")
+            del Lr, keep
+            torch.cuda.synchronize()
+        secondary["configs_quantized_linear"] = cfgs
+
         # small batch (M = 4..32) on the fused projections, int8
         small = {}
         gen = torch.Generator(device=dev)
@@ -503,8 +588,9 @@ def main():
             t = time_events(torch, fw, 10)
             small_wo[str(M)] = {"gbs": round(nbw / (t * 1e-3) / 1e9, 1), "us_per_layer": round(t * 1e3, 2)}
             del keep
-        secondary["small_m_fused_int8"] = small
-        secondary["small_m_weight_only_int8"] = small_wo
+        # (one layer's weights, 218 MB, re-read each replay: partly served by the 256 MB MALL)
+        secondary["small_m_products_only_int8_one_layer"] = small
+        secondary["small_m_weight_only_int8_one_layer"] = small_wo
         log(f"small-M fused {small}")
         log(f"small-M weight-only {small_wo}")
         del wts

@@ -74,22 +74,22 @@ __device__ __forceinline__ int dot16_i8(const v4u& w, const v4u& x, int acc) {
     return acc;
 }
 
-__device__ __forceinline__ float dot4_e4m3(uint32_t w, uint32_t x, float acc) {
-    const v2f w01 = e4m3_unpack2<false>(w), w23 = e4m3_unpack2<true>(w);
-    const v2f x01 = e4m3_unpack2<false>(x), x23 = e4m3_unpack2<true>(x);
-    acc = __builtin_fmaf(w01.x, x01.x, acc);
-    acc = __builtin_fmaf(w01.y, x01.y, acc);
-    acc = __builtin_fmaf(w23.x, x23.x, acc);
-    acc = __builtin_fmaf(w23.y, x23.y, acc);
-    return acc;
+// E4M3 products on the matrix cores, one weight row at a time.  A 16x16x128
+// MFMA whose A operand is this lane's 32 weight bytes and whose B operand is
+// the activation bytes at the same positions returns, on its diagonal,
+// C[i][i] = the sum over the four lanes l with l % 16 == i of their bytewise
+// products (both operands map register bytes to K slots the same way).  The
+// diagonal sits in lanes with (l % 16) / 4 == l / 16, register l % 4.
+__device__ __forceinline__ v4f mfma_e4m3(const v4u& w0, const v4u& w1, const v4u& x0, const v4u& x1, v4f c) {
+    const v8i a = v8i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+    const v8i b = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ float dot16_e4m3(const v4u& w, const v4u& x) {
-    float a = dot4_e4m3(w.x, x.x, 0.0f);
-    float b = dot4_e4m3(w.y, x.y, 0.0f);
-    a = dot4_e4m3(w.z, x.z, a);
-    b = dot4_e4m3(w.w, x.w, b);
-    return a + b;
+__device__ __forceinline__ float mfma16_diag(const v4f& c, int lane) {
+    const int e = lane & 3;
+    const float v = e == 0 ? c.x : (e == 1 ? c.y : (e == 2 ? c.z : c.w));
+    return ((lane & 15) >> 2) == (lane >> 4) ? v : 0.0f;
 }
 
 // V: scheme; KC: 1 KiB slices per row in registers (K <= 1024 KC); R: rows
@@ -102,8 +102,9 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     constexpr bool FP8 = V != VAR_INT8;
     constexpr int CPT = (KC + 1) / 2;
     constexpr int RL = SG ? 2 * R : R;   // weight rows loaded per iteration
+    constexpr int SL = KC;   // 16-byte slots per lane and row
     __shared__ uint32_t red[kThreads / kWave];
-    __shared__ __attribute__((aligned(16))) uint8_t xq[KC * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t xq[SL * 1024];
     __shared__ float gsc[KC * 8];   // block scheme: one scale per 128-input group
 
     const int tid = threadIdx.x;
@@ -134,6 +135,9 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         for (int t = 1; t < kMaxSegments; ++t) i += (t < sa.nseg && r >= sa.start[t]) ? 1 : 0;
         return i;
     };
+    // 16-byte slot j of a row held by this lane, in units of 16 bytes: one wave
+    // load covers the j-th KiB of the row, lane l its bytes at 16 l.
+    auto slot = [&](int j) { return j * kWave + lane; };
     // loaded row r of the group at work item n0: its segment and row within it
     // (items past the wave's range re-read a valid row)
     auto row_of = [&](int r, int n0, int& i, int& local) {
@@ -146,18 +150,28 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
             local = n - sa.start[i];
         }
     };
-    auto load_rows = [&](v4u (&dst)[RL][KC], int n0) {
+    // block FP8: with its weights, the row's weight-block scales, lane l holding
+    // group l (and 64 + l): at most 128 groups (K <= 16384)
+    constexpr int NF = V == VAR_FP8_BLOCK ? (KC > 8 ? 2 : 1) : 1;
+    const int kbs = K >> 7;
+    auto load_rows = [&](v4u (&dst)[RL][SL], uint32_t (&fsw)[RL][NF], int n0) {
 #pragma unroll
         for (int r = 0; r < RL; ++r) {
             int i, local;
             row_of(r, n0, i, local);
             const v4u* wrow = reinterpret_cast<const v4u*>(sa.w[i] + (int64_t)local * K);
 #pragma unroll
-            for (int j = 0; j < KC; ++j) dst[r][j] = __builtin_nontemporal_load(wrow + min(j * kWave + lane, k16 - 1));
+            for (int j = 0; j < SL; ++j) dst[r][j] = __builtin_nontemporal_load(wrow + min(slot(j), k16 - 1));
+            if constexpr (V == VAR_FP8_BLOCK) {
+                const uint16_t* swr = sa.sw[i] + (int64_t)(local >> 7) * kbs;
+#pragma unroll
+                for (int q = 0; q < NF; ++q) fsw[r][q] = swr[min(64 * q + lane, kbs - 1)];
+            }
         }
     };
-    v4u cur[RL][KC];
-    load_rows(cur, rb);     // unconditional: the rounding below only waits for the bf16 row
+    v4u cur[RL][SL];
+    uint32_t fsw[RL][NF];
+    load_rows(cur, fsw, rb);     // unconditional: the rounding below only waits for the bf16 row
 
     // ---- activation rounding into LDS
     if constexpr (V == VAR_FP8_BLOCK) {
@@ -206,17 +220,35 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         }
     }
 
-    v4u xr[KC];
+    v4u xr[SL];
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-        const int o = j * kWave + lane;
+    for (int j = 0; j < SL; ++j) {
+        const int o = slot(j);
         xr[j] = (o < k16) ? *reinterpret_cast<const v4u*>(xq + o * 16) : v4u{0, 0, 0, 0};
     }
     const float s_tok = gsc[0];
-    const int kbs = K >> 7;
+
+    // Block FP8 on the matrix cores needs the four lanes of MFMA row i (lanes
+    // i, i + 16, i + 32, i + 48) to hold one 128-input group: lane l takes the
+    // 16 bytes loaded by lane 4 (l % 16) + l / 16, so row i holds bytes
+    // [64 i, 64 i + 64) of each KiB, half of group i / 2.
+    const int paddr = 4 * (4 * (lane & 15) + (lane >> 4));
+    auto bperm = [&](const v4u& v) {
+        return v4u{(unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)v.x),
+                   (unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)v.y),
+                   (unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)v.z),
+                   (unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)v.w)};
+    };
+    float gx[NF];                  // block FP8: s_x of group l (and 64 + l)
+    if constexpr (V == VAR_FP8_BLOCK) {
+#pragma unroll
+        for (int j = 0; j < SL; ++j) xr[j] = bperm(xr[j]);
+#pragma unroll
+        for (int q = 0; q < NF; ++q) gx[q] = gsc[min(64 * q + lane, kbs - 1)];
+    }
 
     // ---- stream the weight rows: the first group was loaded before the rounding
-    auto process = [&](const v4u (&wr)[RL][KC], int n0) {
+    auto process = [&](const v4u (&wr)[RL][SL], const uint32_t (&fw)[RL][NF], int n0) {
         float facc[RL];
         int iacc[RL];
 #pragma unroll
@@ -227,19 +259,28 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
                 for (int j = 0; j < KC; ++j) a = dot16_i8(wr[r][j], xr[j], a);
                 iacc[r] = wave_sum_i32(a);
             } else if constexpr (V == VAR_FP8_ROW) {
-                float a = 0.0f;
+                v4f c = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < KC; ++j) a += dot16_e4m3(wr[r][j], xr[j]);
-                facc[r] = wave_sum_f32(a);
+                for (int q = 0; q < (SL + 1) / 2; ++q)
+                    c = mfma_e4m3(wr[r][2 * q], 2 * q + 1 < SL ? wr[r][2 * q + 1] : v4u{0, 0, 0, 0}, xr[2 * q],
+                                  2 * q + 1 < SL ? xr[2 * q + 1] : v4u{0, 0, 0, 0}, c);
+                facc[r] = wave_sum_f32(mfma16_diag(c, lane));
             } else {
-                int i, local;
-                row_of(r, n0, i, local);
-                const uint16_t* swr = sa.sw[i] + (int64_t)(local >> 7) * kbs;
+                // one MFMA per KiB (half of its K slots zero): diagonal element i
+                // is half of group 8 q + i / 2, scaled by s_x[group] * s_w[row
+                // block, group] before it is added (groups past K meet zero
+                // activations; their factors are clamped copies)
+                float f[NF];
+#pragma unroll
+                for (int h = 0; h < NF; ++h) f[h] = gx[h] * bf16_lo(fw[r][h]);
                 float a = 0.0f;
 #pragma unroll
-                for (int j = 0; j < KC; ++j) {
-                    const int kb = min(j * kWave + lane, k16 - 1) >> 3;   // slices past K: zero activations
-                    a = __builtin_fmaf(dot16_e4m3(wr[r][j], xr[j]), gsc[kb] * bf16_lo(swr[kb]), a);
+                for (int q = 0; q < SL; ++q) {
+                    const v4f p = mfma_e4m3(bperm(wr[r][q]), v4u{0, 0, 0, 0}, xr[q], v4u{0, 0, 0, 0},
+                                            v4f{0.f, 0.f, 0.f, 0.f});
+                    const int g = (8 * q + ((lane & 15) >> 1)) & 63;   // group 8 q + i / 2, in register q / 8
+                    const float fg = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * g, __float_as_int(f[q / 8])));
+                    a = __builtin_fmaf(mfma16_diag(p, lane), fg, a);
                 }
                 facc[r] = wave_sum_f32(a);
             }
@@ -284,10 +325,10 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
             }
         }
     };
-    if (rb < re) process(cur, rb);
+    if (rb < re) process(cur, fsw, rb);
     for (int n0 = rb + R; n0 < re; n0 += R) {
-        load_rows(cur, n0);
-        process(cur, n0);
+        load_rows(cur, fsw, n0);
+        process(cur, fsw, n0);
     }
 }
 
