@@ -17,8 +17,9 @@
 // counts, so two stages of loads stay in flight while a stage is multiplied.
 // (Direct global->LDS loads were tried: the compiler then drains every load in
 // flight before any LDS read of the tile.)  LDS rows are 128 bytes with the
-// 16-byte chunk index XOR-swizzled by (row & 7), so the MFMA operand reads
-// (eight rows, one logical chunk) hit eight distinct bank groups.
+// 16-byte chunk index XOR-swizzled by swz(row) = (row & 7) ^ ((row >> 3) & 1):
+// an MFMA operand read (one logical chunk of 16 consecutive rows per 16-lane
+// phase) hits 16 distinct 16-byte bank groups.
 //
 // A operand = weight rows (n), B operand = tokens (m): a lane's 16 accumulator
 // values are 16 rows n of one token column m inside one 32-row slab.  For block
@@ -50,6 +51,8 @@ template <> struct LargeAcc<VAR_FP8_ROW> { typedef v16f T; };
 template <> struct LargeAcc<VAR_FP8_BLOCK> { typedef v16f T; };
 
 template <int U> using IC = std::integral_constant<int, U>;
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int V, int BN, int BM, int WN, int WM, bool SG>
 __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
@@ -116,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     int roff[JR];                                          // byte offset of each carried row
 #pragma unroll
     for (int j = 0; j < JR; ++j) roff[j] = ((tid >> 3) + 32 * j) * K;
-    // LDS byte offset of carried row j: row r = tid / 8 + 32 j keeps r & 7
-    const int loff0 = (tid >> 3) * kBK + ((cthr ^ ((tid >> 3) & 7)) << 4);
+    // LDS byte offset of carried row j: row r = tid / 8 + 32 j keeps swz(r)
+    const int loff0 = (tid >> 3) * kBK + ((cthr ^ swz(tid >> 3)) << 4);
     const int nk = (K + kBK - 1) / kBK;
     const int kbs = K >> 7;
 
@@ -220,12 +223,12 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
 #pragma unroll
                 for (int i = 0; i < TN; ++i) {
                     const int r = arow0 + i * 32;
-                    a[sub][i] = *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ (r & 7)) << 4));
+                    a[sub][i] = *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ swz(r)) << 4));
                 }
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
                     const int r = brow0 + j * 32;
-                    bb[sub][j] = *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ (r & 7)) << 4));
+                    bb[sub][j] = *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ swz(r)) << 4));
                 }
             };
             auto mm = [&](int sub) {
@@ -259,15 +262,15 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
 #pragma unroll
                 for (int i = 0; i < TN; ++i) {
                     const int r = arow0 + i * 32;
-                    const v4i lo = *reinterpret_cast<const v4i*>(base + r * kBK + ((c0 ^ (r & 7)) << 4));
-                    const v4i hi = *reinterpret_cast<const v4i*>(base + r * kBK + (((c0 + 1) ^ (r & 7)) << 4));
+                    const v4i lo = *reinterpret_cast<const v4i*>(base + r * kBK + ((c0 ^ swz(r)) << 4));
+                    const v4i hi = *reinterpret_cast<const v4i*>(base + r * kBK + (((c0 + 1) ^ swz(r)) << 4));
                     a[sub][i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 }
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
                     const int r = brow0 + j * 32;
-                    const v4i lo = *reinterpret_cast<const v4i*>(base + r * kBK + ((c0 ^ (r & 7)) << 4));
-                    const v4i hi = *reinterpret_cast<const v4i*>(base + r * kBK + (((c0 + 1) ^ (r & 7)) << 4));
+                    const v4i lo = *reinterpret_cast<const v4i*>(base + r * kBK + ((c0 ^ swz(r)) << 4));
+                    const v4i hi = *reinterpret_cast<const v4i*>(base + r * kBK + (((c0 + 1) ^ swz(r)) << 4));
                     bb[sub][j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 }
             };
