@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     const uint16_t* __restrict__ x, int K, SegmentArgs sa, int mode,
     uint8_t* __restrict__ qx_out, float* __restrict__ sx_out) {
     constexpr bool FP8 = V != VAR_INT8;
-    constexpr int CPT = (KC + 1) / 2;
+    constexpr int CPT = (128 * KC + kThreads - 1) / kThreads;
     constexpr int RL = SG ? 2 * R : R;   // weight rows loaded per iteration
     constexpr int SL = KC;   // 16-byte slots per lane and row
     __shared__ uint32_t red[kThreads / kWave];
@@ -194,7 +194,9 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         amax = wave_max_u32(amax);
         if (lane == 0) red[wave] = amax;
         __syncthreads();
-        amax = max(max(red[0], red[1]), max(red[2], red[3]));
+        amax = red[0];
+#pragma unroll
+        for (int i = 1; i < kThreads / kWave; ++i) amax = max(amax, red[i]);
         float s, inv;
         scales_from_absmax<FP8>(amax, s, inv);
         if (tid == 0) gsc[0] = s;
@@ -361,7 +363,7 @@ void launch_kc(int R, int grid, hipStream_t st, const uint16_t* x, int K, const 
 void decode_launch_shape(int64_t ntot, int64_t K, int* R, int* grid) {
     const int64_t kc = (K + 1023) / 1024;
     *R = (kc > 4 && kc <= 8) ? 2 : 1;
-    const int64_t rows = 4 * (kc <= 4 ? 1 : 2);         // rows per workgroup of four wavefronts
+    const int64_t rows = (kThreads / kWave) * (kc <= 4 ? 1 : 2);   // rows per workgroup
     const int64_t g = (ntot + rows - 1) / rows;
     *grid = (int)(g < 1 ? 1 : g);
 }
