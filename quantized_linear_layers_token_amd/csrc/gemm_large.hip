@@ -174,10 +174,16 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     auto write = [&](auto set, auto buf, int s) {
         const v4u(&r)[CH] = decltype(set)::value ? ry : rx;
         uint8_t* base = lds + decltype(buf)::value * STAGE;
-        const bool ok = s * kBK + cthr * 16 < K;           // false in a ragged last stage and past the end
+        if ((K & (kBK - 1)) == 0) {
+            // whole stages only: a stage past the end is written but never multiplied
 #pragma unroll
-        for (int j = 0; j < CH; ++j)
-            *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = ok ? r[j] : v4u{0, 0, 0, 0};
+            for (int j = 0; j < CH; ++j) *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = r[j];
+        } else {
+            const bool ok = s * kBK + cthr * 16 < K;       // false in the ragged last stage and past the end
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = ok ? r[j] : v4u{0, 0, 0, 0};
+        }
         if constexpr (V == VAR_FP8_BLOCK) {
             const float(&fxs)[TM] = decltype(set)::value ? fxy : fxx;
             const float(&fws)[TN] = decltype(set)::value ? fwy : fwx;
@@ -213,7 +219,11 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     issue_all(IC<1>{}, 1);
     __syncthreads();
 
+    // A wave issues its stage's MFMAs at raised priority (back to normal for the
+    // LDS writes and the barrier), so a SIMD shared by two workgroups keeps
+    // feeding the matrix core while the other wave is in its write phase.
     auto compute = [&](auto buf, const float (&fx)[TM], const float (&fw)[TN], auto&& hk) {
+        __builtin_amdgcn_s_setprio(1);
         const uint8_t* base = lds + decltype(buf)::value * STAGE;
         if constexpr (V == VAR_INT8) {
             constexpr int SUB = 4;                    // 32-byte K sub-steps per stage
@@ -326,13 +336,26 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
         compute(IC<0>{}, fx0, fw0, [&](int h) { hook(IC<0>{}, kt + 2, h); });
+        __builtin_amdgcn_s_setprio(0);
         write(IC<1>{}, IC<1>{}, kt + 1);
         __syncthreads();
         compute(IC<1>{}, fx1, fw1, [&](int h) { hook(IC<1>{}, kt + 3, h); });
+        __builtin_amdgcn_s_setprio(0);
         write(IC<0>{}, IC<0>{}, kt + 2);
         __syncthreads();
     }
-    if (kt < nk) compute(IC<0>{}, fx0, fw0, [&](int) {});
+    if (kt < nk) {
+        compute(IC<0>{}, fx0, fw0, [&](int) {});
+        // The epilogue reads the accumulators right after these MFMAs.  With the
+        // wave at raised priority, the last register of the last 32x32x64 E4M3
+        // MFMA was read before that MFMA had written it (the value lacked
+        // exactly that MFMA's contribution) although the compiler had padded
+        // the read: 64 more idle issue slots, once per tile.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
 
     // Epilogue.  Lane l, accumulator element e of MFMA tile (i, j):
     //   n = n0 + wn*SN + i*32 + 8*(e/4) + 4*(l/32) + e%4,   m = m0 + wm*SM + j*32 + l%32,
