@@ -204,11 +204,14 @@ typedef struct qlin_segment {
  * (W8A8 model card, intro and "Loading"; Qwen3 8B FP8 card, "Loading").
  *
  * M == 1 and K <= 16384: one launch -- every workgroup rounds the row into LDS
- * and streams its share of all segments' weight rows; q_x / s_x may be null, and
- * when given receive the codes and scale(s).  Otherwise q_x (M*K bytes) and s_x
- * ([M] or [M, K/128] f32) are required caller-owned staging buffers: one
- * quantizer launch, then one product launch covering every segment (regime by
- * M).  The segments array is read during the call only. */
+ * and streams its share of all segments' weight rows.  M == 2 and K <= 16384
+ * (FP8_BLOCK: K <= 8192): one launch as well -- persistent workgroups round
+ * both tokens into LDS once and stream the weight rows one at a time.  In these
+ * one-launch cases q_x / s_x may be null, and when given receive the codes and
+ * scale(s).  Otherwise q_x (M*K bytes) and s_x ([M] or [M, K/128] f32) are
+ * required caller-owned staging buffers: one quantizer launch, then one product
+ * launch covering every segment (regime by M).  The segments array is read
+ * during the call only. */
 qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
                         const qlin_segment* segments, int32_t nseg, qlin_out out,
                         void* q_x, float* s_x, hipStream_t stream);

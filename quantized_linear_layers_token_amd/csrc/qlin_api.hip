@@ -154,12 +154,12 @@ extern "C" {
 
 qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
                         int32_t nseg, qlin_out out, void* q_x, float* s_x, hipStream_t stream) {
-    const bool fused = (M == 1) && (K <= qlin::kDecodeMaxK);
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
+                        : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
+    const bool fused = ((M == 1) && (K <= qlin::kDecodeMaxK)) || qlin::linear_tokens_fits(variant, M, K);
     bool noop = false;
     const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, q_x, s_x, fused, &noop);
     if (st != QLIN_OK || noop) return st;
-    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
-                        : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
     // the non-empty segments, packed
     qlin::SegmentArgs sa{};
     int n = 0, k = 0;
@@ -174,8 +174,11 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
     }
     sa.nseg = k;
     for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
-    if (fused)
+    if (fused && M == 1)
         return hip_status(qlin::launch_linear_decode(variant, x, K, sa, (int)out, static_cast<uint8_t*>(q_x), s_x,
+                                                     stream));
+    if (fused)
+        return hip_status(qlin::launch_linear_tokens(variant, x, M, K, sa, (int)out, static_cast<uint8_t*>(q_x), s_x,
                                                      stream));
     hipError_t e;
     if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);

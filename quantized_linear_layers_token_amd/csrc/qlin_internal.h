@@ -57,6 +57,15 @@ hipError_t launch_linear_decode(int variant, const uint16_t* x, int64_t K, const
                                 uint8_t* qx, float* sx, hipStream_t st);
 constexpr int64_t kDecodeMaxK = 16384;   // fused one-row path keeps the quantized row in LDS/registers
 
+// Fused product for a few tokens streaming the weights row by row (every
+// segment of sa in one launch); fits when the tokens' codes fit in LDS.  The
+// kernel supports up to 8 tokens; the dispatch uses it where it was measured
+// faster than quantizer + matrix-core kernel: 2 tokens.
+constexpr int64_t kLinearTokensMaxM = 2;
+bool linear_tokens_fits(int variant, int64_t M, int64_t K);
+hipError_t launch_linear_tokens(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa, int mode,
+                                uint8_t* qx, float* sx, hipStream_t st);
+
 // Weight-only ("equivalent") numerics: bf16 activations times dequantized
 // weights, every segment of sa in one launch.  M <= 32.
 constexpr int64_t kWeightOnlyRowMaxK = 16384;   // one-token kernel keeps the bf16 row in LDS

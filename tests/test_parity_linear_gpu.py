@@ -153,3 +153,74 @@ def test_linear_ragged_segments_tiled(scheme):
         else:
             ye = exact(scheme, qx_ref, sx_ref, qw, sw)
             assert np.max(np.abs(y - ye)) <= 4e-3 * np.max(np.abs(ye))
+
+
+# two tokens: one launch (persistent workgroups round the tokens into LDS once
+# and stream the weight rows); the staging buffers are optional there
+TOKEN_CASES = [
+    # (M, K, segment widths)
+    (2, 128, [128]),
+    (2, 16384, [128, 256]),              # longest rows
+    (2, 1152, [256, 384, 128, 640]),     # four segments, K not a multiple of 1 KiB
+    (2, 4096, [4096, 1024, 1024]),       # q, k, v
+    (2, 14336, [512]),                   # down-shaped rows
+]
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R, FP8B])
+@pytest.mark.parametrize("M,K,ns", TOKEN_CASES)
+def test_linear_few_tokens_one_launch(scheme, M, K, ns):
+    x = W.x_bf16(7700 + M + K, M, K)
+    segs = make_segments(scheme, 7710 + K + M, ns, K)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
+    # block FP8 rows beyond 8 KiB take the staged path: there staging is required
+    one_launch = not (scheme == FP8B and K > 8192)
+    if not one_launch:
+        with pytest.raises(Q().QlinError):
+            run_linear_opt(scheme, x, segs, BF16, False)
+    for staged in ((False, True) if one_launch else (True,)):
+        ys, qx, sx = run_linear_opt(scheme, x, segs, BF16, staged)
+        if staged:
+            if scheme == W8A8:
+                assert np.array_equal(qx.view(np.int8), qx_ref)
+            else:
+                assert e4m3_equal_mod_zero(qx, qx_ref)
+            assert np.array_equal(sx.reshape(sx_ref.shape).view(np.uint32), sx_ref.view(np.uint32))
+        for (qw, sw), y in zip(segs, ys):
+            ye = exact(scheme, qx_ref, sx_ref, qw, sw)
+            assert_within_tol(y, ye, f"{M} tokens scheme {scheme} staged {staged}")
+            if scheme == W8A8:
+                assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
+
+
+def test_linear_few_tokens_ragged_rows_exact():
+    # ragged widths and the int32 accumulator of every row (two tokens; three
+    # takes the staged path)
+    for M in (2,):
+        K = 1040
+        x = W.x_bf16(7800 + M, M, K)
+        segs = make_segments(W8A8, 7810 + M, [200, 72, 1, 33], K)
+        qx_ref, _ = O.quant_act_int8(x)
+        ys, _, _ = run_linear_opt(W8A8, x, segs, I32, False)
+        for (qw, _), y in zip(segs, ys):
+            assert np.array_equal(y, O.contract_int8(qx_ref, qw))
+
+
+def run_linear_opt(scheme, x, segs, out, staged):
+    """qlin_linear with staging buffers only when asked for."""
+    torch = torch_mod()
+    M, K = x.shape
+    esz = 2 if out == BF16 else 4
+    ys = [empty(torch, (M * qw.shape[0] * esz + 64,), torch.uint8, fill=0xFF) for qw, _ in segs]
+    qx = sx = None
+    if staged:
+        qx = empty(torch, (M, K), torch.uint8, fill=0x55)
+        sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32, fill=0x55)
+    Q().qlin_linear(scheme, dev(x), [(dev(qw), dev(sw), y) for (qw, sw), y in zip(segs, ys)], out=out, q_x=qx, s_x=sx)
+    res = []
+    for (qw, _), y in zip(segs, ys):
+        raw = host(y)
+        n = qw.shape[0]
+        assert (raw[M * n * esz:] == 0xFF).all(), "guard band overwritten"
+        res.append(raw[:M * n * esz].view({BF16: np.uint16, I32: np.int32, F32: np.float32}[out]).reshape(M, n))
+    return res, (None if qx is None else host(qx)), (None if sx is None else host(sx))
