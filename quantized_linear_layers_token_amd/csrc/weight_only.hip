@@ -12,7 +12,9 @@
 // One token (M = 1, K <= 16384): wo_gemv_kernel streams each weight byte once
 // like the quantized one-row product; the workgroup stages the bf16 row in
 // LDS and every wavefront keeps the 32-byte input slices matching its 16-byte
-// weight slices in registers.  Int8 codes and E4M3 codes widen exactly to f32.
+// weight slices in registers.  The codes widen exactly to bf16 and meet the
+// inputs on the matrix cores (the diagonal of a 16x16x32 bf16 MFMA per 8
+// codes), so the vector ALUs only widen.
 //
 // 2..32 tokens (or longer K): wo_small_kernel, the small-M weight stream with
 // the codes widened exactly to bf16 in registers and multiplied on the matrix
@@ -36,29 +38,30 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // code b of a packed dword, widened exactly
 __device__ __forceinline__ float i8_at(uint32_t w, int b) { return (float)((int)(w << (24 - 8 * b)) >> 24); }
 
-// sum over 16 positions of code * input: w = 16 codes, xa / xb = inputs 0..7 / 8..15 (bf16 pairs)
+// 8 codes (two dwords) widened exactly to bf16
 template <int V>
-__device__ __forceinline__ float dot16_codes_bf16(const v4u& w, const v4u& xa, const v4u& xb) {
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-    const uint32_t xd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    float a = 0.0f, b = 0.0f;
+__device__ __forceinline__ v8bf codes_to_bf16(uint32_t w0, uint32_t w1) {
+    float f[8];
+    if constexpr (V == VAR_INT8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t x01 = xd[2 * i], x23 = xd[2 * i + 1];
-        if constexpr (V == VAR_INT8) {
-            a = __builtin_fmaf(i8_at(wd[i], 0), bf16_lo(x01), a);
-            b = __builtin_fmaf(i8_at(wd[i], 1), bf16_hi(x01), b);
-            a = __builtin_fmaf(i8_at(wd[i], 2), bf16_lo(x23), a);
-            b = __builtin_fmaf(i8_at(wd[i], 3), bf16_hi(x23), b);
-        } else {
-            const v2f w01 = e4m3_unpack2<false>(wd[i]), w23 = e4m3_unpack2<true>(wd[i]);
-            a = __builtin_fmaf(w01.x, bf16_lo(x01), a);
-            b = __builtin_fmaf(w01.y, bf16_hi(x01), b);
-            a = __builtin_fmaf(w23.x, bf16_lo(x23), a);
-            b = __builtin_fmaf(w23.y, bf16_hi(x23), b);
+        for (int b = 0; b < 4; ++b) {
+            f[b] = i8_at(w0, b);
+            f[4 + b] = i8_at(w1, b);
         }
+    } else {
+        const v2f a = e4m3_unpack2<false>(w0), b = e4m3_unpack2<true>(w0);
+        const v2f c = e4m3_unpack2<false>(w1), d = e4m3_unpack2<true>(w1);
+        f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+        f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
     }
-    return a + b;
+    // every such value has at most 8 significant bits: the high half of its
+    // f32 pattern is its bf16 pattern
+    v4u p;
+    p.x = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    p.y = __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+    p.z = __builtin_amdgcn_perm(__float_as_uint(f[5]), __float_as_uint(f[4]), 0x07060302u);
+    p.w = __builtin_amdgcn_perm(__float_as_uint(f[7]), __float_as_uint(f[6]), 0x07060302u);
+    return __builtin_bit_cast(v8bf, p);
 }
 
 // ---------------------------------------------------------------------------
@@ -117,16 +120,34 @@ __global__ __launch_bounds__(kThreads) void wo_gemv_kernel(const uint16_t* __res
         if (c < nchunks) *reinterpret_cast<v4u*>(xs + c * 16) = xb[j];
     }
     __syncthreads();
-    // slice o = j*64 + lane: inputs 16 o .. 16 o + 15; slices past K are zero
+    // The products run on the matrix cores: one 16x16x32 bf16 MFMA per 8 codes,
+    // A = this lane's codes widened to bf16, B = the inputs at the same
+    // positions, so the diagonal C[i][i] sums the products of the four lanes
+    // with l % 16 == i.  Block FP8: lane l takes the codes loaded by lane
+    // 4 (l % 16) + l / 16 (and reads the matching inputs), so diagonal
+    // element i holds half of one 128-input group.
+    const int src = V == VAR_FP8_BLOCK ? 4 * (lane & 15) + (lane >> 4) : lane;
+    const int paddr = 4 * src;
+    // slice o = j*64 + src: inputs 16 o .. 16 o + 15; slices past K are zero
     v4u xa[KC], xc[KC];
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-        const int o = j * kWave + lane;
+        const int o = j * kWave + src;
         const bool ok = o < k16;
         xa[j] = ok ? *reinterpret_cast<const v4u*>(xs + o * 32) : v4u{0, 0, 0, 0};
         xc[j] = ok ? *reinterpret_cast<const v4u*>(xs + o * 32 + 16) : v4u{0, 0, 0, 0};
     }
     const int kbs = K >> 7;
+    auto slice_mfma = [&](const v4u& w, int j, v4f c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16<V>(w.x, w.y), __builtin_bit_cast(v8bf, xa[j]), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16<V>(w.z, w.w), __builtin_bit_cast(v8bf, xc[j]), c, 0, 0,
+                                                       0);
+    };
+    auto diag = [&](const v4f& c) {
+        const int e = lane & 3;
+        const float v = e == 0 ? c.x : (e == 1 ? c.y : (e == 2 ? c.z : c.w));
+        return ((lane & 15) >> 2) == (lane >> 4) ? v : 0.0f;
+    };
 
     auto process = [&](const v4u (&wr)[R][KC], int n0) {
         float facc[R];
@@ -139,12 +160,19 @@ __global__ __launch_bounds__(kThreads) void wo_gemv_kernel(const uint16_t* __res
                 const uint16_t* swr = sa.sw[i] + (int64_t)((n - sa.start[i]) >> 7) * kbs;
 #pragma unroll
                 for (int j = 0; j < KC; ++j) {
-                    const int kb = min(j * kWave + lane, k16 - 1) >> 3;   // 16-wide slices stay inside a block
-                    a = __builtin_fmaf(dot16_codes_bf16<V>(wr[r][j], xa[j], xc[j]), bf16_lo(swr[kb]), a);
+                    const v4u w = {(unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)wr[r][j].x),
+                                   (unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)wr[r][j].y),
+                                   (unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)wr[r][j].z),
+                                   (unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)wr[r][j].w)};
+                    const v4f p = slice_mfma(w, j, v4f{0.f, 0.f, 0.f, 0.f});
+                    const int g = min(8 * j + ((lane & 15) >> 1), kbs - 1);   // the diagonal element's group
+                    a = __builtin_fmaf(diag(p), bf16_lo(swr[g]), a);
                 }
             } else {
+                v4f c = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < KC; ++j) a += dot16_codes_bf16<V>(wr[r][j], xa[j], xc[j]);
+                for (int j = 0; j < KC; ++j) c = slice_mfma(wr[r][j], j, c);
+                a = diag(c);
             }
             facc[r] = wave_sum_f32(a);
         }
@@ -169,32 +197,6 @@ __global__ __launch_bounds__(kThreads) void wo_gemv_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------
 // 2..32 tokens
 // ---------------------------------------------------------------------------
-
-// 8 codes (two dwords) widened exactly to bf16
-template <int V>
-__device__ __forceinline__ v8bf codes_to_bf16(uint32_t w0, uint32_t w1) {
-    float f[8];
-    if constexpr (V == VAR_INT8) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            f[b] = i8_at(w0, b);
-            f[4 + b] = i8_at(w1, b);
-        }
-    } else {
-        const v2f a = e4m3_unpack2<false>(w0), b = e4m3_unpack2<true>(w0);
-        const v2f c = e4m3_unpack2<false>(w1), d = e4m3_unpack2<true>(w1);
-        f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
-        f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
-    }
-    // every such value has at most 8 significant bits: the high half of its
-    // f32 pattern is its bf16 pattern
-    v4u p;
-    p.x = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-    p.y = __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
-    p.z = __builtin_amdgcn_perm(__float_as_uint(f[5]), __float_as_uint(f[4]), 0x07060302u);
-    p.w = __builtin_amdgcn_perm(__float_as_uint(f[7]), __float_as_uint(f[6]), 0x07060302u);
-    return __builtin_bit_cast(v8bf, p);
-}
 
 constexpr int kWoBatch = 2;         // K steps per load batch (two batches in flight)
 
@@ -350,8 +352,11 @@ template <int V>
 void launch_wo_gemv_v(const uint16_t* x, int64_t K, const SegmentArgs& sa, int mode, hipStream_t st) {
     const int64_t ntot = sa.start[sa.nseg];
     const int64_t kc = (K + 1023) / 1024;
-    const int R = kc <= 8 ? 2 : 1;                 // a workgroup covers 8 rows either way
-    const int grid = (int)std::max<int64_t>(1, (ntot + 7) / 8);
+    // as the quantized one-row launch: one row per wavefront for rows up to
+    // 4 KiB, two read together up to 8 KiB, two in turn beyond
+    const int R = (kc > 4 && kc <= 8) ? 2 : 1;
+    const int64_t rows = kc <= 4 ? 4 : 8;          // rows per workgroup of four wavefronts
+    const int grid = (int)std::max<int64_t>(1, (ntot + rows - 1) / rows);
     const int k = (int)K;
     if (kc <= 1) launch_wo_gemv_kc<V, 1>(R, grid, st, x, k, sa, mode);
     else if (kc <= 2) launch_wo_gemv_kc<V, 2>(R, grid, st, x, k, sa, mode);
