@@ -2,8 +2,11 @@
 // 8B FP8 card, "Loading": inputs of at most 32 rows go to the matrix units).
 //
 // The weights dominate the traffic (arithmetic intensity <= 2M ops/byte), so
-// the kernel is a weight stream: every weight byte is loaded from HBM once,
-// straight into MFMA operand registers (no LDS staging).
+// the kernel is a weight stream: every weight byte is loaded from HBM once.
+// Loads cover whole 128-byte lines (8 rows per instruction) and each K step
+// goes through a per-wave LDS buffer into the MFMA register layout: loading
+// that layout directly (16 rows x 64 bytes per instruction) left the kernel
+// bound by the L1 address path.
 //
 //   workgroup = one tile of 16 weight rows (output channels) x the full K,
 //               split over NW wavefronts along K (each owns a contiguous run
@@ -49,7 +52,13 @@ template <int V, int MT, int NW, int RT, bool SG>
 __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode) {
     typedef typename SmallAcc<V>::T Acc;
-    __shared__ Acc red[NW][RT * MT][kWave];
+    // per-wave transpose buffer for one K step (RT weight tiles + MT token
+    // tiles, 16 rows x 128 bytes each), reused for the split-K reduction
+    constexpr int TPB = (RT + MT) * 2048;
+    constexpr int SMEM = NW * TPB > (int)(NW * RT * MT * kWave * sizeof(Acc)) ? NW * TPB
+                                                                              : (int)(NW * RT * MT * kWave * sizeof(Acc));
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+    auto red = reinterpret_cast<Acc(*)[RT * MT][kWave]>(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -92,15 +101,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     // SG: the up rows with the same indices (segment 1, equal width)
     const __amdgpu_buffer_rsrc_t du = uniform_rsrc(sa.w[SG ? 1 : 0] + (int64_t)n0 * K, SG ? min(TR, N - n0) * K : 0);
     const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(qx, M * K);
-    // Lane (r16, grp) takes bytes [16 grp, 16 grp + 16) and [64 + 16 grp, ...)
-    // of each 128-byte step, so one load instruction covers one contiguous
-    // 64-byte piece of each of 16 rows.  Both operands use the same
-    // assignment, so the contraction is unchanged by it.  The RT weight tiles
-    // of a wavefront share its token registers.
-    const int woff = r16 * K + grp * 16;
-    int xoff[MT];
+    // Loads cover whole 128-byte lines: lane l reads 16 bytes 16 (l % 8) of row
+    // l / 8 (and of row 8 + l / 8) of a tile; the K step is then transposed
+    // through this wave's LDS buffer into the MFMA layout, lane l holding
+    // bytes [16 g, +16) and [64 + 16 g, +16) of row l % 16, g = l / 16 (both
+    // operands the same way, so the contraction is unchanged).  The RT weight
+    // tiles of a wavefront share its token fragments.
+    const int lr = lane >> 3, lp = lane & 7;
+    const int woff = lr * K + lp * 16;
+    int xoff[MT][2];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) xoff[t] = (t * 16 + r16 < M) ? (t * 16 + r16) * K + grp * 16 : kOOB;
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int m = t * 16 + 8 * h + lr;
+            xoff[t][h] = m < M ? m * K + lp * 16 : kOOB;
+        }
+    auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+    uint8_t* tpw = smem + wave * TPB;
+    const int wr_off0 = lr * 128 + ((lp ^ swz(lr)) << 4);             // LDS position of this lane's piece, row lr
+    const int wr_off1 = (lr + 8) * 128 + ((lp ^ swz(lr + 8)) << 4);    // ... row lr + 8
+    const int rd_off0 = r16 * 128 + ((grp ^ swz(r16)) << 4);          // MFMA layout: piece g of row l % 16
+    const int rd_off1 = r16 * 128 + (((4 + grp) ^ swz(r16)) << 4);    // ... piece 4 + g
 
     const int kbs = K >> 7;
     const uint16_t* swblk = sw + (int64_t)(n0 >> 7) * kbs;  // block FP8: the tile's 128-row block
@@ -123,21 +145,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int s = s0 + u;
-            const int k = s * 128 + grp * 16;
-            const bool ok0 = (s < s_end) && (k < K);
-            const bool ok1 = (s < s_end) && (k + 64 < K);
+            const int k = s * 128 + lp * 16;
+            const bool ok = (s < s_end) && (k < K);
             // weights stream once: non-temporal
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const bool up = SG && r >= RH;
                 const int o = woff + (up ? r - RH : r) * 16 * K + s * 128;
-                wa[bi][u][r][0] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok0 ? o : kOOB, 0, kAuxStream);
-                wa[bi][u][r][1] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok1 ? o + 64 : kOOB, 0, kAuxStream);
+                wa[bi][u][r][0] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok ? o : kOOB, 0, kAuxStream);
+                wa[bi][u][r][1] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok ? o + 8 * K : kOOB, 0, kAuxStream);
             }
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                xa[bi][u][t][0] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok0 ? xoff[t] + s * 128 : kOOB, 0, 0);
-                xa[bi][u][t][1] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok1 ? xoff[t] + s * 128 + 64 : kOOB, 0, 0);
+                xa[bi][u][t][0] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok && xoff[t][0] != kOOB ? xoff[t][0] + s * 128 : kOOB, 0, 0);
+                xa[bi][u][t][1] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok && xoff[t][1] != kOOB ? xoff[t][1] + s * 128 : kOOB, 0, 0);
             }
             if constexpr (V == VAR_FP8_BLOCK) {
                 const int sb = min(s, s_end - 1);
@@ -152,11 +173,33 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
         constexpr int bi = decltype(bufc)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            // transpose this step through the wave's LDS buffer
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                *reinterpret_cast<v4u*>(tpw + r * 2048 + wr_off0) = wa[bi][u][r][0];
+                *reinterpret_cast<v4u*>(tpw + r * 2048 + wr_off1) = wa[bi][u][r][1];
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                *reinterpret_cast<v4u*>(tpw + (RT + t) * 2048 + wr_off0) = xa[bi][u][t][0];
+                *reinterpret_cast<v4u*>(tpw + (RT + t) * 2048 + wr_off1) = xa[bi][u][t][1];
+            }
+            v4u ta[RT][2], tx[MT][2];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                ta[r][0] = *reinterpret_cast<const v4u*>(tpw + r * 2048 + rd_off0);
+                ta[r][1] = *reinterpret_cast<const v4u*>(tpw + r * 2048 + rd_off1);
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                tx[t][0] = *reinterpret_cast<const v4u*>(tpw + (RT + t) * 2048 + rd_off0);
+                tx[t][1] = *reinterpret_cast<const v4u*>(tpw + (RT + t) * 2048 + rd_off1);
+            }
 #pragma unroll
             for (int r = 0; r < RT; ++r)
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
-                    const v4u w0 = wa[bi][u][r][0], w1 = wa[bi][u][r][1], x0 = xa[bi][u][t][0], x1 = xa[bi][u][t][1];
+                    const v4u w0 = ta[r][0], w1 = ta[r][1], x0 = tx[t][0], x1 = tx[t][1];
                     if constexpr (V == VAR_INT8) {
                         acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, w0),
                                                                           __builtin_bit_cast(v4i, x0), acc[r][t], 0, 0, 0);
@@ -194,6 +237,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
         compute(IC<1>{}, s0 + U);
     }
     if (s0 < s_end) compute(IC<0>{}, s0);
+    __syncthreads();   // every wave is done with its transpose buffer before the reduction reuses it
 
 #pragma unroll
     for (int r = 0; r < RT; ++r)
