@@ -204,9 +204,10 @@ typedef struct qlin_segment {
  * (W8A8 model card, intro and "Loading"; Qwen3 8B FP8 card, "Loading").
  *
  * M == 1 and K <= 16384: one launch -- every workgroup rounds the row into LDS
- * and streams its share of all segments' weight rows.  M == 2 and K <= 16384
- * (FP8_BLOCK: K <= 8192): one launch as well -- persistent workgroups round
- * both tokens into LDS once and stream the weight rows one at a time.  In these
+ * and streams its share of all segments' weight rows.  M == 2, K <= 16384
+ * (FP8_BLOCK: K <= 8192) and at most 64 MiB of weights in the call: one launch
+ * as well -- persistent workgroups round both tokens into LDS once and stream
+ * the weight rows one at a time.  In these
  * one-launch cases q_x / s_x may be null, and when given receive the codes and
  * scale(s).  Otherwise q_x (M*K bytes) and s_x ([M] or [M, K/128] f32) are
  * required caller-owned staging buffers: one quantizer launch, then one product

@@ -265,17 +265,20 @@ hipError_t launch_mt(int M, int grid, hipStream_t st, const uint16_t* x, int K, 
 }  // namespace
 
 // Block FP8 rows longer than 8 KiB measured slower here (the per-KiB MFMA,
-// permutation and scale traffic of every token) than on the staged path.
-bool linear_tokens_fits(int variant, int64_t M, int64_t K) {
+// permutation and scale traffic of every token) than on the staged path, and
+// so did calls streaming more than 64 MB of weights (the gate/up pair), where
+// the quantizer launch is amortized and the matrix-core kernel streams faster.
+bool linear_tokens_fits(int variant, int64_t M, int64_t K, int64_t rows) {
     const int64_t kc = (K + 1023) / 1024;
     if (variant == VAR_FP8_BLOCK && kc > 8) return false;
+    if (rows * K > (int64_t(64) << 20)) return false;
     return M >= 2 && M <= kLinearTokensMaxM && kc <= 16 && kLinearTokensMaxM * kc <= 64;
 }
 
 hipError_t launch_linear_tokens(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa, int mode,
                                 uint8_t* qx, float* sx, hipStream_t st) {
-    if (!linear_tokens_fits(variant, M, K)) return hipErrorInvalidValue;
     const int64_t ntot = sa.start[sa.nseg];
+    if (!linear_tokens_fits(variant, M, K, ntot)) return hipErrorInvalidValue;
     // persistent: two workgroups per CU at most, never more than one row per wavefront
     const int64_t g = (ntot + kWaves - 1) / kWaves;
     const int grid = (int)(g < 512 ? (g < 1 ? 1 : g) : 512);

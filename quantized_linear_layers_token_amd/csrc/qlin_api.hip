@@ -156,7 +156,10 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
                         int32_t nseg, qlin_out out, void* q_x, float* s_x, hipStream_t stream) {
     const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
                         : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
-    const bool fused = ((M == 1) && (K <= qlin::kDecodeMaxK)) || qlin::linear_tokens_fits(variant, M, K);
+    int64_t rows = 0;   // weight rows of the call (validated by check_linear below)
+    if (segments != nullptr && nseg >= 1 && nseg <= QLIN_MAX_SEGMENTS)
+        for (int i = 0; i < nseg; ++i) rows += segments[i].n > 0 ? segments[i].n : 0;
+    const bool fused = ((M == 1) && (K <= qlin::kDecodeMaxK)) || qlin::linear_tokens_fits(variant, M, K, rows);
     bool noop = false;
     const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, q_x, s_x, fused, &noop);
     if (st != QLIN_OK || noop) return st;

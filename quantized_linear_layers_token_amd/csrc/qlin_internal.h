@@ -62,7 +62,7 @@ constexpr int64_t kDecodeMaxK = 16384;   // fused one-row path keeps the quantiz
 // kernel supports up to 8 tokens; the dispatch uses it where it was measured
 // faster than quantizer + matrix-core kernel: 2 tokens.
 constexpr int64_t kLinearTokensMaxM = 2;
-bool linear_tokens_fits(int variant, int64_t M, int64_t K);
+bool linear_tokens_fits(int variant, int64_t M, int64_t K, int64_t rows);
 hipError_t launch_linear_tokens(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa, int mode,
                                 uint8_t* qx, float* sx, hipStream_t st);
 

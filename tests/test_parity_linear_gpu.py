@@ -224,3 +224,18 @@ def run_linear_opt(scheme, x, segs, out, staged):
         assert (raw[M * n * esz:] == 0xFF).all(), "guard band overwritten"
         res.append(raw[:M * n * esz].view({BF16: np.uint16, I32: np.int32, F32: np.float32}[out]).reshape(M, n))
     return res, (None if qx is None else host(qx)), (None if sx is None else host(sx))
+
+
+def test_linear_two_tokens_large_call_takes_staged_path():
+    # more than 64 MiB of weights at two tokens (the gate/up pair): quantizer +
+    # matrix-core kernel, so the staging buffers are required
+    M, K, ns = 2, 4096, [14336, 14336]
+    x = W.x_bf16(7900, M, K)
+    segs = make_segments(W8A8, 7910, ns, K)
+    with pytest.raises(Q().QlinError):
+        run_linear_opt(W8A8, x, segs, BF16, False)
+    ys, qx, _ = run_linear_opt(W8A8, x, segs, BF16, True)
+    qx_ref, sx_ref = O.quant_act_int8(x)
+    assert np.array_equal(qx.view(np.int8), qx_ref)
+    for (qw, sw), y in zip(segs, ys):
+        assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
