@@ -203,7 +203,13 @@ constexpr int kWoBatch = 2;         // K steps per load batch (two batches in fl
 template <int V, int MT, int NW>
 __global__ __launch_bounds__(NW * 64) void wo_small_kernel(const uint16_t* __restrict__ x, SegmentArgs sa, int M,
                                                            int K, int mode) {
-    __shared__ v4f red[NW][MT][kWave];
+    // per-wave transpose buffer for one K step: 16 weight rows x 128 bytes,
+    // then MT token tiles of 16 tokens x 256 bytes (bf16); reused for the
+    // split-K reduction
+    constexpr int TPB = 2048 + MT * 4096;
+    constexpr int SMEM = NW * TPB > (int)(NW * MT * kWave * sizeof(v4f)) ? NW * TPB : (int)(NW * MT * kWave * sizeof(v4f));
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+    auto red = reinterpret_cast<v4f(*)[MT][kWave]>(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -239,10 +245,33 @@ __global__ __launch_bounds__(NW * 64) void wo_small_kernel(const uint16_t* __res
     // zero through the descriptors.
     const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(16, N - n0) * K);
     const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(x, M * K * 2);
-    const int woff = r16 * K + grp * 16;
-    int xoff[MT];
+    // Loads cover whole 128-byte lines and go through this wave's LDS buffer
+    // into the MFMA layout above: weights 8 rows x 128 bytes per instruction
+    // (lane l: row l / 8, bytes 16 (l % 8)), inputs 4 tokens x 256 bytes per
+    // instruction (lane l: token l / 16, bytes 16 (l % 16)).
+    const int lr = lane >> 3, lp = lane & 7;
+    const int woff = lr * K + lp * 16;
+    int xoff[MT][4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) xoff[t] = (t * 16 + r16 < M) ? ((t * 16 + r16) * K + grp * 16) * 2 : kOOB;
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = t * 16 + 4 * q + (lane >> 4);
+            xoff[t][q] = m < M ? (m * K) * 2 + (lane & 15) * 16 : kOOB;
+        }
+    auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+    uint8_t* tpw = smem + wave * TPB;
+    const int ww0 = lr * 128 + ((lp ^ swz(lr)) << 4), ww1 = (lr + 8) * 128 + ((lp ^ swz(lr + 8)) << 4);
+    const int wr0 = r16 * 128 + ((grp ^ swz(r16)) << 4), wr1 = r16 * 128 + (((4 + grp) ^ swz(r16)) << 4);
+    // token rows of 256 bytes, 16-byte chunk c of token m at chunk c ^ (m % 16)
+    int xw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = 4 * q + (lane >> 4);
+        xw[q] = m * 256 + (((lane & 15) ^ m) << 4);
+    }
+    const int xr[4] = {r16 * 256 + (((2 * grp) ^ r16) << 4), r16 * 256 + (((2 * grp + 1) ^ r16) << 4),
+                       r16 * 256 + (((8 + 2 * grp) ^ r16) << 4), r16 * 256 + (((9 + 2 * grp) ^ r16) << 4)};
     const int kbs = K >> 7;
     const uint16_t* swblk = sw + (int64_t)(n0 >> 7) * kbs;  // block: the tile's 128-row block
 
@@ -258,19 +287,16 @@ __global__ __launch_bounds__(NW * 64) void wo_small_kernel(const uint16_t* __res
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int s = s0 + u;
-            const int k = s * 128 + grp * 16;
-            const bool ok0 = (s < s_end) && (k < K);
-            const bool ok1 = (s < s_end) && (k + 64 < K);
-            wa[bi][u][0] = __builtin_amdgcn_raw_buffer_load_b128(dw, ok0 ? woff + s * 128 : kOOB, 0, kAuxStream);
-            wa[bi][u][1] = __builtin_amdgcn_raw_buffer_load_b128(dw, ok1 ? woff + s * 128 + 64 : kOOB, 0, kAuxStream);
+            const bool okw = (s < s_end) && (s * 128 + lp * 16 < K);
+            const bool okx = (s < s_end) && (s * 128 + (lane & 15) * 8 < K);
+            wa[bi][u][0] = __builtin_amdgcn_raw_buffer_load_b128(dw, okw ? woff + s * 128 : kOOB, 0, kAuxStream);
+            wa[bi][u][1] = __builtin_amdgcn_raw_buffer_load_b128(dw, okw ? woff + 8 * K + s * 128 : kOOB, 0, kAuxStream);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int o = xoff[t] + s * 256;
-                xa[bi][u][t][0] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok0 ? o : kOOB, 0, 0);
-                xa[bi][u][t][1] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok0 ? o + 16 : kOOB, 0, 0);
-                xa[bi][u][t][2] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok1 ? o + 128 : kOOB, 0, 0);
-                xa[bi][u][t][3] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok1 ? o + 144 : kOOB, 0, 0);
-            }
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xa[bi][u][t][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                        dx, okx && xoff[t][q] != kOOB ? xoff[t][q] + s * 256 : kOOB, 0, 0);
             if constexpr (V == VAR_FP8_BLOCK) fw[bi][u] = bf16_lo(swblk[min(s, s_end - 1)]);
         }
     };
@@ -278,7 +304,19 @@ __global__ __launch_bounds__(NW * 64) void wo_small_kernel(const uint16_t* __res
         constexpr int bi = decltype(bufc)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const v4u w0 = wa[bi][u][0], w1 = wa[bi][u][1];
+            // transpose this step through the wave's LDS buffer
+            *reinterpret_cast<v4u*>(tpw + ww0) = wa[bi][u][0];
+            *reinterpret_cast<v4u*>(tpw + ww1) = wa[bi][u][1];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) *reinterpret_cast<v4u*>(tpw + 2048 + t * 4096 + xw[q]) = xa[bi][u][t][q];
+            const v4u w0 = *reinterpret_cast<const v4u*>(tpw + wr0), w1 = *reinterpret_cast<const v4u*>(tpw + wr1);
+            v4u tx[MT][4];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tx[t][i] = *reinterpret_cast<const v4u*>(tpw + 2048 + t * 4096 + xr[i]);
             const v8bf a[4] = {codes_to_bf16<V>(w0.x, w0.y), codes_to_bf16<V>(w0.z, w0.w),
                                codes_to_bf16<V>(w1.x, w1.y), codes_to_bf16<V>(w1.z, w1.w)};
 #pragma unroll
@@ -286,8 +324,7 @@ __global__ __launch_bounds__(NW * 64) void wo_small_kernel(const uint16_t* __res
                 v4f p = V == VAR_FP8_BLOCK ? v4f{0.f, 0.f, 0.f, 0.f} : acc[t];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], __builtin_bit_cast(v8bf, xa[bi][u][t][i]), p, 0,
-                                                                0, 0);
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], __builtin_bit_cast(v8bf, tx[t][i]), p, 0, 0, 0);
                 if constexpr (V == VAR_FP8_BLOCK) {
                     if (s0 + u < s_end) {
                         const float f = fw[bi][u];
@@ -314,6 +351,7 @@ __global__ __launch_bounds__(NW * 64) void wo_small_kernel(const uint16_t* __res
         compute(IC<1>{}, s0 + U);
     }
     if (s0 < s_end) compute(IC<0>{}, s0);
+    __syncthreads();   // every wave is done with its transpose buffer before the reduction reuses it
 
 #pragma unroll
     for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
