@@ -85,7 +85,11 @@ typedef enum qlin_path {
     QLIN_PATH_LARGE_256X128 = 4,
     QLIN_PATH_LARGE_128X128 = 5,
     QLIN_PATH_LARGE_128X64 = 6,
-    QLIN_PATH_LARGE_128X256 = 7
+    QLIN_PATH_LARGE_128X256 = 7,
+    /* the same tiles with 8 wavefronts: two groups of four split the K stages
+     * of one tile and add their partial sums before the epilogue */
+    QLIN_PATH_LARGE_128X128_K2 = 8,
+    QLIN_PATH_LARGE_128X64_K2 = 9
 } qlin_path;
 
 /* ---------------------------------------------------------------------- */

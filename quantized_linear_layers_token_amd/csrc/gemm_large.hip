@@ -30,6 +30,12 @@
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8; tile ids are
 // assigned so that tiles sharing a weight panel are consecutive on one XCD.
 //
+// K groups (KG = 2): 512 threads in two groups of four wavefronts; group g
+// multiplies stages g, g + 2, ... of the same tile from its own pair of LDS
+// buffers, and group 1 adds its partial sums into group 0's through LDS before
+// the epilogue (int32 sums stay exact).  With too few tiles for two
+// workgroups per CU, a tile then still keeps two wavefronts per SIMD.
+//
 // SwiGLU mode (SG): the BN weight rows of a tile are BN/2 gate rows j0.. and
 // the up rows with the same indices; the bf16 epilogue tile in LDS then holds
 // gate and up of each (j, m), and the store pass writes
@@ -54,12 +60,14 @@ template <int U> using IC = std::integral_constant<int, U>;
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int V, int BN, int BM, int WN, int WM, bool SG>
-__global__ __launch_bounds__(kThreads) void gemm_large_kernel(
+template <int V, int BN, int BM, int WN, int WM, bool SG, int KG>
+__global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa,
     int M, int K, int mode, int tiles_m, int tiles_n) {
     typedef typename LargeAcc<V>::T Acc;
-    static_assert(WN * WM == 4, "four wavefronts");
+    static_assert(WN * WM == 4, "four wavefronts per K group");
+    static_assert(KG == 1 || KG == 2, "one or two K groups");
+    constexpr int NTH = kThreads * KG;
     constexpr int SN = BN / WN, SM = BM / WM;              // wave sub-tile
     constexpr int TN = SN / 32, TM = SM / 32;              // 32x32 MFMA tiles per wave
     constexpr int ROWS = BN + BM;                          // LDS rows per stage (weights first)
@@ -68,12 +76,14 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     static_assert(ROWS * 8 % kThreads == 0 && TN >= 1 && TM >= 1 && SN % 32 == 0 && SM % 32 == 0, "tile");
     // MFMA groups per stage at which loads are issued (see compute)
     constexpr int HOOKS = V == VAR_INT8 ? 4 * TN : (V == VAR_FP8_ROW ? 2 * TN : TN * TM);
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[KG * 2 * STAGE];
     __shared__ float s_w_t[BN], s_x_t[BM];                // rowwise schemes: this tile's scales
 
     const int tid = threadIdx.x;
+    const int gtid = tid & (kThreads - 1);                 // thread index inside its K group
+    const int grp = __builtin_amdgcn_readfirstlane(tid / kThreads);
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(gtid >> 6);
     const int wn = wave / WM, wm = wave % WM;
 
     const int ntiles = tiles_m * tiles_n;
@@ -112,16 +122,22 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     // or M lie outside the descriptor's range and read as zero.
     constexpr int JW = BN / 32, JX = BM / 32, JR = JW > JX ? JW : JX;
     static_assert(JW + JX == CH, "chunk split");
-    const int cthr = tid & 7;
+    const int cthr = gtid & 7;
     const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(PR, N - n0) * K);
     const __amdgpu_buffer_rsrc_t du = uniform_rsrc(sa.w[SG ? 1 : 0] + (int64_t)n0 * K, SG ? min(PR, N - n0) * K : 0);
     const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(qx + (int64_t)m0 * K, min(BM, M - m0) * K);
     int roff[JR];                                          // byte offset of each carried row
 #pragma unroll
-    for (int j = 0; j < JR; ++j) roff[j] = ((tid >> 3) + 32 * j) * K;
+    for (int j = 0; j < JR; ++j) roff[j] = ((gtid >> 3) + 32 * j) * K;
     // LDS byte offset of carried row j: row r = tid / 8 + 32 j keeps swz(r)
-    const int loff0 = (tid >> 3) * kBK + ((cthr ^ swz(tid >> 3)) << 4);
+    const int loff0 = (gtid >> 3) * kBK + ((cthr ^ swz(gtid >> 3)) << 4);
     const int nk = (K + kBK - 1) / kBK;
+    // K group g multiplies stages g, g + KG, g + 2 KG, ... from its own pair of
+    // LDS buffers; both groups run the same number of steps (barriers are
+    // shared), a step past the last stage multiplies a zero stage.
+    const int nko = (nk + KG - 1) / KG;
+    uint8_t* const glds = lds + grp * 2 * STAGE;
+    auto gs = [&](int i) { return KG * i + grp; };
     const int kbs = K >> 7;
 
     // Register staging: stage s is loaded into register set s % 2 while stage
@@ -173,8 +189,12 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     };
     auto write = [&](auto set, auto buf, int s) {
         const v4u(&r)[CH] = decltype(set)::value ? ry : rx;
-        uint8_t* base = lds + decltype(buf)::value * STAGE;
-        if ((K & (kBK - 1)) == 0) {
+        uint8_t* base = glds + decltype(buf)::value * STAGE;
+        if (KG > 1 && s >= nk) {
+            // a K group's step past the last stage: zeros
+#pragma unroll
+            for (int j = 0; j < CH; ++j) *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = v4u{0, 0, 0, 0};
+        } else if ((K & (kBK - 1)) == 0) {
             // whole stages only: a stage past the end is written but never multiplied
 #pragma unroll
             for (int j = 0; j < CH; ++j) *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = r[j];
@@ -196,6 +216,11 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
         }
     };
 
+    // With 512 threads a wave may hold 256 registers.  Unless AGPRs are known
+    // to be in use, the compiler then takes all 256 as VGPRs, selects the
+    // VGPR form of the MFMAs and spills; naming one AGPR keeps the
+    // accumulators in AGPRs (128 + 128).
+    if constexpr (KG > 1) asm volatile("" ::: "a0");
     Acc acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
@@ -208,15 +233,15 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
 
     if constexpr (V != VAR_FP8_BLOCK) {
         // the epilogue's scales, staged once
-        for (int i = tid; i < BN; i += kThreads)
+        for (int i = tid; i < BN; i += NTH)
             s_w_t[i] = (SG && i >= PR) ? bf16_lo(sw_u[min(n0 + i - PR, N - 1)]) : bf16_lo(sw[min(n0 + i, N - 1)]);
-        for (int i = tid; i < BM; i += kThreads) s_x_t[i] = sx[min(m0 + i, M - 1)];
+        for (int i = tid; i < BM; i += NTH) s_x_t[i] = sx[min(m0 + i, M - 1)];
     }
 
     // prologue: stage 0 in LDS buffer 0, stage 1 in flight
-    issue_all(IC<0>{}, 0);
-    write(IC<0>{}, IC<0>{}, 0);
-    issue_all(IC<1>{}, 1);
+    issue_all(IC<0>{}, gs(0));
+    write(IC<0>{}, IC<0>{}, gs(0));
+    issue_all(IC<1>{}, gs(1));
     __syncthreads();
 
     // A wave issues its stage's MFMAs at raised priority (back to normal for the
@@ -224,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     // feeding the matrix core while the other wave is in its write phase.
     auto compute = [&](auto buf, const float (&fx)[TM], const float (&fw)[TN], auto&& hk) {
         __builtin_amdgcn_s_setprio(1);
-        const uint8_t* base = lds + decltype(buf)::value * STAGE;
+        const uint8_t* base = glds + decltype(buf)::value * STAGE;
         if constexpr (V == VAR_INT8) {
             constexpr int SUB = 4;                    // 32-byte K sub-steps per stage
             v4i a[SUB][TN], bb[SUB][TM];
@@ -334,17 +359,17 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     // writes zeros to a buffer that is not multiplied again (a conditional
     // load makes the compiler assume the shallower pipeline everywhere).
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        compute(IC<0>{}, fx0, fw0, [&](int h) { hook(IC<0>{}, kt + 2, h); });
+    for (; kt + 1 < nko; kt += 2) {
+        compute(IC<0>{}, fx0, fw0, [&](int h) { hook(IC<0>{}, gs(kt + 2), h); });
         __builtin_amdgcn_s_setprio(0);
-        write(IC<1>{}, IC<1>{}, kt + 1);
+        write(IC<1>{}, IC<1>{}, gs(kt + 1));
         __syncthreads();
-        compute(IC<1>{}, fx1, fw1, [&](int h) { hook(IC<1>{}, kt + 3, h); });
+        compute(IC<1>{}, fx1, fw1, [&](int h) { hook(IC<1>{}, gs(kt + 3), h); });
         __builtin_amdgcn_s_setprio(0);
-        write(IC<0>{}, IC<0>{}, kt + 2);
+        write(IC<0>{}, IC<0>{}, gs(kt + 2));
         __syncthreads();
     }
-    if (kt < nk) {
+    if (kt < nko) {
         compute(IC<0>{}, fx0, fw0, [&](int) {});
         // The epilogue reads the accumulators right after these MFMAs.  With the
         // wave at raised priority, the last register of the last 32x32x64 E4M3
@@ -356,6 +381,40 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
+
+    if constexpr (KG == 2) {
+        // group 1 hands its partial sums to group 0 through LDS (one dword per
+        // lane and accumulator element, lane-contiguous), group 0 adds them
+        constexpr int NACC = TN * TM * 16;
+        static_assert(4 * NACC * 64 * 4 <= (int)sizeof(lds), "partials fit the stage buffers");
+        uint32_t* part = reinterpret_cast<uint32_t*>(lds) + wave * NACC * 64 + lane;
+        __syncthreads();                                   // both groups are done with their stages
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        // (a bit cast of the vector element itself reads element 0)
+                        if constexpr (V == VAR_INT8) part[((i * TM + j) * 16 + e) * 64] = (uint32_t)acc[i][j][e];
+                        else part[((i * TM + j) * 16 + e) * 64] = __float_as_uint(acc[i][j][e]);
+                    }
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const uint32_t v = part[((i * TM + j) * 16 + e) * 64];
+                        if constexpr (V == VAR_INT8) acc[i][j][e] += (int)v;
+                        else acc[i][j][e] += __uint_as_float(v);
+                    }
+        }
+    }
 
     // Epilogue.  Lane l, accumulator element e of MFMA tile (i, j):
     //   n = n0 + wn*SN + i*32 + 8*(e/4) + 4*(l/32) + e%4,   m = m0 + wm*SM + j*32 + l%32,
@@ -371,6 +430,7 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
         constexpr int PITCH = BN * 2 + 16;
         static_assert(BM * PITCH <= (int)sizeof(lds), "bf16 staging tile fits the stage buffers");
         __syncthreads();                                   // every wave is done with the last stage
+        if (grp == 0) {
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
             const int ml = wm * SM + j * 32 + (lane & 31);
@@ -392,11 +452,12 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
                     *reinterpret_cast<v2u*>(lds + ml * PITCH + nl * 2) = v2u{lo, hi};
                 }
         }
+        }
         __syncthreads();
         if constexpr (SG) {
             // gate of (row, j) at column j - n0, up at column PR + j - n0
             constexpr int CPH = PR * 2 / 16;               // 16-byte pieces per h row
-            for (int id = tid; id < BM * CPH; id += kThreads) {
+            for (int id = tid; id < BM * CPH; id += NTH) {
                 const int row = id / CPH, c = id % CPH;
                 const int m = m0 + row, j = n0 + 8 * c;
                 if (m >= M || j >= N) continue;
@@ -421,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
         }
         constexpr int CPR = BN * 2 / 16;                   // 16-byte pieces per tile row
 #pragma unroll 4
-        for (int id = tid; id < BM * CPR; id += kThreads) {
+        for (int id = tid; id < BM * CPR; id += NTH) {
             const int row = id / CPR, c = id % CPR;
             const int m = m0 + row, n = n0 + 8 * c;
             if (m < M && n < N)
@@ -432,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     }
     // Other outputs: straight from the accumulators, one 8-byte (bf16) or
     // 16-byte (f32 / i32) store per four outputs when the row length allows it.
+    if (grp != 0) return;
     const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -474,20 +536,20 @@ __global__ __launch_bounds__(kThreads) void gemm_large_kernel(
     }
 }
 
-template <int V, int BN, int BM, int WN, int WM>
+template <int V, int BN, int BM, int WN, int WM, int KG = 1>
 hipError_t launch_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K, int mode,
                        hipStream_t st) {
     const int tm = (int)((M + BM - 1) / BM);
-    dim3 block(kThreads);
+    dim3 block(kThreads * KG);
     if (mode == OUT_SWIGLU) {
         const int tn = (sa.start[1] + BN / 2 - 1) / (BN / 2);
-        hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, true>), dim3((unsigned)(tm * tn)), block, 0, st, qx,
+        hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, true, KG>), dim3((unsigned)(tm * tn)), block, 0, st, qx,
                            sx, sa, (int)M, (int)K, mode, tm, tn);
         return hipGetLastError();
     }
     int tn = 0;
     for (int i = 0; i < sa.nseg; ++i) tn += (sa.start[i + 1] - sa.start[i] + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, false>), dim3((unsigned)(tm * tn)), block, 0, st, qx, sx,
+    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, false, KG>), dim3((unsigned)(tm * tn)), block, 0, st, qx, sx,
                        sa, (int)M, (int)K, mode, tm, tn);
     return hipGetLastError();
 }
@@ -500,25 +562,32 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
         case kTile128x128: return launch_tile<V, 128, 128, 2, 2>(qx, sx, sa, M, K, mode, st);
         case kTile128x64: return launch_tile<V, 128, 64, 2, 2>(qx, sx, sa, M, K, mode, st);
         case kTile128x256: return launch_tile<V, 128, 256, 2, 2>(qx, sx, sa, M, K, mode, st);
+        case kTile128x128K2: return launch_tile<V, 128, 128, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
+        case kTile128x64K2: return launch_tile<V, 128, 64, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-// Tile choice (measured on the Llama-8B projections at 512 and 1024 tokens):
-// 128 x 128 once it yields three quarters of a workgroup per CU, else
-// 128 x 64 to keep every CU busy.  The 256-row tiles need more load bandwidth
-// per CU than the vector memory path sustains next to the LDS traffic, and
-// lose on every shape measured.  Block FP8 scales every stage's partial
-// products on the vector ALUs; its smaller wave tile measured fastest.
+// Tile choice, from timings of every tile on the Llama-8B projections at 256,
+// 512 and 1024 tokens (t = number of 128 x 128 tiles, 256 CUs):
+//   t >= 384: 128 x 128, two workgroups share a CU;
+//   192 <= t < 384: 128 x 128 with two K groups (8 wavefronts, one tile per
+//     CU, two wavefronts per SIMD);
+//   t < 192: 128 x 64 with two K groups.
+// Block FP8 scales every stage's partial products on the vector ALUs; its
+// 128 x 128 tile with two K groups needs more registers than 8 wavefronts
+// leave (it spills), so it keeps 128 x 64, with two K groups below 192 tiles.
+// The 256-row tiles need more load bandwidth per CU than the vector memory
+// path sustains next to the LDS traffic, and lose on every shape measured.
 int large_tile_config(int variant, int64_t M, const SegmentArgs& sa) {
-    if (variant == VAR_FP8_BLOCK) return kTile128x64;
     int64_t panels = 0;
     for (int i = 0; i < sa.nseg; ++i) panels += (sa.start[i + 1] - sa.start[i] + 127) / 128;
-    const int64_t cus = 256;
-    if (((M + 127) / 128) * panels >= cus * 3 / 4) return kTile128x128;
-    return kTile128x64;
+    const int64_t t = ((M + 127) / 128) * panels;
+    if (variant == VAR_FP8_BLOCK) return t < 192 ? kTile128x64K2 : kTile128x64;
+    if (t >= 384) return kTile128x128;
+    return t >= 192 ? kTile128x128K2 : kTile128x64K2;
 }
 
 hipError_t launch_gemm_large_cfg(int cfg, int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa,

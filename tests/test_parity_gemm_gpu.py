@@ -319,7 +319,8 @@ def test_fp8_mfma_accumulation_model():
 # Every fixed output tile of the tiled GEMM, on shapes spanning several tiles
 # with ragged M, N and K edges, one- to three-stage K (pipeline prologue and the
 # odd last stage) and tile counts that do and do not divide by the 8 XCDs.
-TILE_PATHS = [4, 5, 6, 7]      # 256x128, 128x128, 128x64, 128x256 (weight rows x tokens)
+TILE_PATHS = [4, 5, 6, 7, 8, 9]   # 256x128, 128x128, 128x64, 128x256 (weight rows x tokens), then
+                                # 128x128 and 128x64 with two K groups (odd stage counts: K = 1040, 384)
 TILE_SHAPES = [(300, 600, 1040), (129, 257, 16), (40, 130, 384), (512, 1024, 128), (260, 384, 256)]
 TILE_BLOCK_SHAPES = [(300, 640, 1152), (129, 256, 128), (40, 128, 384), (512, 1024, 256)]
 
