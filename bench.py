@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--pmc-workload", action="store_true",
                     help="for hardware-counter runs: a 1 GiB copy (counter calibration), then two eager "
                          "decode steps; prints no JSON")
+    ap.add_argument("--prefill-workload", action="store_true",
+                    help="for kernel traces of the prefill path: the M=512 Llama layer set (4 layers, one "
+                         "qlin_linear call per input group), int8 then FP8 rowwise, three eager passes each; "
+                         "prints no JSON")
     return ap.parse_args()
 
 
@@ -423,6 +427,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     use_graph = not args.no_graph
+
+    if args.prefill_workload:
+        for variant in ("int8", "fp8_row"):
+            _, _, fused, _, ops, keep = prefill_layer_set(
+                torch, Q, W, variant, 512, 4, dev, {"int8": 300, "fp8_row": 400}[variant] + 512)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                fused.run()
+            torch.cuda.synchronize()
+            log(f"prefill workload {variant}: M=512, 4 layers, {len(fused.calls)} calls per pass x3, "
+                f"{ops} ops per pass")
+            del keep, fused
+        return
 
     # ---- headline: decode, M = 1, 32 distinct layers -------------------------
     log("building decode workload (32 layers, int8)")
