@@ -211,7 +211,9 @@ typedef struct qlin_segment {
  * and streams its share of all segments' weight rows.  M == 2, K <= 16384
  * (FP8_BLOCK: K <= 8192) and at most 64 MiB of weights in the call: one launch
  * as well -- persistent workgroups round both tokens into LDS once and stream
- * the weight rows one at a time.  In these
+ * the weight rows one at a time.  Otherwise 2 <= M <= 4 with K <= 4096: one
+ * launch of the small-M matrix-core kernel, every workgroup rounding the
+ * tokens into its LDS.  In these
  * one-launch cases q_x / s_x may be null, and when given receive the codes and
  * scale(s).  Otherwise q_x (M*K bytes) and s_x ([M] or [M, K/128] f32) are
  * required caller-owned staging buffers: one quantizer launch, then one product

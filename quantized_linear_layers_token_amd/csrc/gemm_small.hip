@@ -26,6 +26,12 @@
 //               weight scales, per-128-input activation scales).
 //   split-K   = the NW partial tiles are summed through LDS, then the scale
 //               epilogue writes y.
+//   fused     = (FU, at most 4 tokens of at most 4096 inputs) the kernel takes
+//               the bf16 activations: each of the first M wavefronts rounds
+//               one token (the standalone quantizers' arithmetic) into the
+//               workgroup's LDS while the first weight batch is in flight,
+//               and the token operand is read from there; no quantizer
+//               launch precedes the product.
 //   SwiGLU    = (SG) the first RT/2 MFMA row tiles are gate rows j0.., the
 //               other RT/2 the up rows with the same indices: after the
 //               reduction a lane holds gate and up of the same (j, m) and
@@ -34,6 +40,7 @@
 
 #include "qlin_device.h"
 #include "qlin_internal.h"
+#include "qlin_rows.h"
 
 namespace qlin {
 
@@ -48,17 +55,32 @@ template <int V> struct SmallAcc { typedef v4i T; };
 template <> struct SmallAcc<VAR_FP8_ROW> { typedef v4f T; };
 template <> struct SmallAcc<VAR_FP8_BLOCK> { typedef v4f T; };
 
-template <int V, int MT, int NW, int RT, bool SG>
+// FU (fused): the kernel takes the bf16 input and rounds its M <= kSmallFusedMaxM
+// tokens itself: waves 0 .. M - 1 each round one token into this workgroup's
+// LDS (per token, or per 128-input group for block FP8; the standalone
+// quantizers' arithmetic), while the first weight batch is in flight; the
+// MFMA token operand is then read from there.  Workgroup 0 also fills the
+// optional staging buffers qx_out / sx_out.
+template <int V, int MT, int NW, int RT, bool SG, bool FU = false>
 __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
-    const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode) {
+    const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode,
+    const uint16_t* __restrict__ xbf, uint8_t* __restrict__ qx_out, float* __restrict__ sx_out) {
     typedef typename SmallAcc<V>::T Acc;
+    static_assert(!FU || (MT == 1 && !SG), "fused rounding: one token tile, no SwiGLU");
     // per-wave transpose buffer for one K step (RT weight tiles + MT token
     // tiles, 16 rows x 128 bytes each), reused for the split-K reduction
-    constexpr int TPB = (RT + MT) * 2048;
+    constexpr int TPB = (RT + (FU ? 0 : MT)) * 2048;
     constexpr int SMEM = NW * TPB > (int)(NW * RT * MT * kWave * sizeof(Acc)) ? NW * TPB
                                                                               : (int)(NW * RT * MT * kWave * sizeof(Acc));
     __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
     auto red = reinterpret_cast<Acc(*)[RT * MT][kWave]>(smem);
+    // FU: per token its scale (or one per 128-input group) and its codes,
+    // rows of XS bytes (K rounded up to a 128-byte step, zero past K, + 64 so
+    // that the four rows fall on distinct LDS bank groups)
+    extern __shared__ __attribute__((aligned(16))) uint8_t fdyn[];
+    float* const fsc = reinterpret_cast<float*>(fdyn);
+    uint8_t* const xq = fdyn + kSmallFusedScaleBytes;
+    const int XS = ((K + 127) & ~127) + 64;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -155,17 +177,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                 wa[bi][u][r][0] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok ? o : kOOB, 0, kAuxStream);
                 wa[bi][u][r][1] = __builtin_amdgcn_raw_buffer_load_b128(up ? du : dw, ok ? o + 8 * K : kOOB, 0, kAuxStream);
             }
+            if constexpr (!FU) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                xa[bi][u][t][0] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok && xoff[t][0] != kOOB ? xoff[t][0] + s * 128 : kOOB, 0, 0);
-                xa[bi][u][t][1] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok && xoff[t][1] != kOOB ? xoff[t][1] + s * 128 : kOOB, 0, 0);
+                for (int t = 0; t < MT; ++t) {
+                    xa[bi][u][t][0] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok && xoff[t][0] != kOOB ? xoff[t][0] + s * 128 : kOOB, 0, 0);
+                    xa[bi][u][t][1] = __builtin_amdgcn_raw_buffer_load_b128(dx, ok && xoff[t][1] != kOOB ? xoff[t][1] + s * 128 : kOOB, 0, 0);
+                }
             }
             if constexpr (V == VAR_FP8_BLOCK) {
                 const int sb = min(s, s_end - 1);
                 fw[bi][u][0] = bf16_lo(swblk[sb]);
                 if constexpr (SG) fw[bi][u][1] = bf16_lo(swblk_u[sb]);
+                if constexpr (!FU) {
 #pragma unroll
-                for (int t = 0; t < MT; ++t) fx[bi][u][t] = sx[(int64_t)min(t * 16 + r16, M - 1) * kbs + sb];
+                    for (int t = 0; t < MT; ++t) fx[bi][u][t] = sx[(int64_t)min(t * 16 + r16, M - 1) * kbs + sb];
+                }
             }
         }
     };
@@ -179,10 +205,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                 *reinterpret_cast<v4u*>(tpw + r * 2048 + wr_off0) = wa[bi][u][r][0];
                 *reinterpret_cast<v4u*>(tpw + r * 2048 + wr_off1) = wa[bi][u][r][1];
             }
+            if constexpr (!FU) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                *reinterpret_cast<v4u*>(tpw + (RT + t) * 2048 + wr_off0) = xa[bi][u][t][0];
-                *reinterpret_cast<v4u*>(tpw + (RT + t) * 2048 + wr_off1) = xa[bi][u][t][1];
+                for (int t = 0; t < MT; ++t) {
+                    *reinterpret_cast<v4u*>(tpw + (RT + t) * 2048 + wr_off0) = xa[bi][u][t][0];
+                    *reinterpret_cast<v4u*>(tpw + (RT + t) * 2048 + wr_off1) = xa[bi][u][t][1];
+                }
             }
             v4u ta[RT][2], tx[MT][2];
 #pragma unroll
@@ -190,10 +218,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                 ta[r][0] = *reinterpret_cast<const v4u*>(tpw + r * 2048 + rd_off0);
                 ta[r][1] = *reinterpret_cast<const v4u*>(tpw + r * 2048 + rd_off1);
             }
+            if constexpr (FU) {
+                // token r16's bytes [16 g, +16) and [64 + 16 g, +16) of this step
+                const int s = s0 + u;
+                const bool tok = r16 < M && s < nsteps;
+                const uint8_t* p = xq + r16 * XS + s * 128 + 16 * grp;
+                tx[0][0] = tok ? *reinterpret_cast<const v4u*>(p) : v4u{0, 0, 0, 0};
+                tx[0][1] = tok ? *reinterpret_cast<const v4u*>(p + 64) : v4u{0, 0, 0, 0};
+            } else {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                tx[t][0] = *reinterpret_cast<const v4u*>(tpw + (RT + t) * 2048 + rd_off0);
-                tx[t][1] = *reinterpret_cast<const v4u*>(tpw + (RT + t) * 2048 + rd_off1);
+                for (int t = 0; t < MT; ++t) {
+                    tx[t][0] = *reinterpret_cast<const v4u*>(tpw + (RT + t) * 2048 + rd_off0);
+                    tx[t][1] = *reinterpret_cast<const v4u*>(tpw + (RT + t) * 2048 + rd_off1);
+                }
             }
 #pragma unroll
             for (int r = 0; r < RT; ++r)
@@ -214,7 +251,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                             const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                             if (s0 + u < s_end) {
-                                const float f = fx[bi][u][t] * fw[bi][u][(SG && r >= RH) ? 1 : 0];
+                                const float fxv = FU ? fsc[min(r16, M - 1) * kSmallFusedGroups + min(s0 + u, s_end - 1)]
+                                                     : fx[bi][u][t];
+                                const float f = fxv * fw[bi][u][(SG && r >= RH) ? 1 : 0];
                                 acc[r][t].x = __builtin_fmaf(p.x, f, acc[r][t].x);
                                 acc[r][t].y = __builtin_fmaf(p.y, f, acc[r][t].y);
                                 acc[r][t].z = __builtin_fmaf(p.z, f, acc[r][t].z);
@@ -227,6 +266,64 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     };
 
     issue(IC<0>{}, s_begin);
+    if constexpr (FU) {
+        // round the tokens while the first weight batch is in flight; a lane
+        // holds chunks lane + 64 j of its token (K <= 4096: at most 8)
+        const int nch = K >> 3;                            // 16-byte chunks of 8 bf16
+        if (wave < M) {
+            const int t = wave;
+            const v4u* xr = reinterpret_cast<const v4u*>(xbf + (int64_t)t * K);
+            uint8_t* row = xq + t * XS;
+            const bool stage = qx_out != nullptr && blockIdx.x == 0;
+            v4u v[kSmallFusedChunks];
+#pragma unroll
+            for (int j = 0; j < kSmallFusedChunks; ++j) {
+                const int c = lane + kWave * j;
+                v[j] = c < nch ? xr[c] : v4u{0, 0, 0, 0};
+            }
+            if constexpr (V == VAR_FP8_BLOCK) {
+                // chunks 64 j + 16 r .. + 15 are one 128-input group: one DPP row
+#pragma unroll
+                for (int j = 0; j < kSmallFusedChunks; ++j) {
+                    const int c = lane + kWave * j;
+                    float sg, inv;
+                    scales_from_absmax<true>(row_max_u32(chunk_absmax(v[j])), sg, inv);
+                    if (c < nch) {
+                        const v2u q = quant8<true>(v[j], inv);
+                        *reinterpret_cast<v2u*>(row + 8 * c) = q;
+                        if (stage) *reinterpret_cast<v2u*>(qx_out + (int64_t)t * K + 8 * c) = q;
+                        if ((lane & 15) == 0) {
+                            fsc[t * kSmallFusedGroups + (c >> 4)] = sg;
+                            if (stage) sx_out[(int64_t)t * kbs + (c >> 4)] = sg;
+                        }
+                    }
+                }
+            } else {
+                uint32_t amax = 0;
+#pragma unroll
+                for (int j = 0; j < kSmallFusedChunks; ++j) amax = max(amax, chunk_absmax(v[j]));
+                float sc, inv;
+                scales_from_absmax<V != VAR_INT8>(wave_max_u32(amax), sc, inv);
+#pragma unroll
+                for (int j = 0; j < kSmallFusedChunks; ++j) {
+                    const int c = lane + kWave * j;
+                    if (c < nch) {
+                        const v2u q = quant8<V != VAR_INT8>(v[j], inv);
+                        *reinterpret_cast<v2u*>(row + 8 * c) = q;
+                        if (stage) *reinterpret_cast<v2u*>(qx_out + (int64_t)t * K + 8 * c) = q;
+                    }
+                }
+                if (lane == 0) {
+                    fsc[t] = sc;
+                    if (stage) sx_out[t] = sc;
+                }
+            }
+            // zeros from K to the end of the last 128-byte step
+            for (int b = K + 16 * lane; b < ((K + 127) & ~127); b += 16 * kWave)
+                *reinterpret_cast<v4u*>(row + b) = v4u{0, 0, 0, 0};
+        }
+        __syncthreads();
+    }
     int s0 = s_begin;
     for (; s0 + U < s_end; s0 += 2 * U) {                 // at least two batches left
         issue(IC<1>{}, s0 + U);
@@ -295,8 +392,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                 const int n = n0 + 16 * r + (l >> 4) * 4 + e;
                 if (n < N) {
                     const int64_t idx = (int64_t)m * N + n;
-                    if constexpr (V == VAR_INT8) store_rowwise_i32acc(y, idx, sum[e], sx[m], sw[n], mode);
-                    else if constexpr (V == VAR_FP8_ROW) store_f32(y, idx, sum[e] * (sx[m] * bf16_lo(sw[n])), mode);
+                    const float sxm = FU ? fsc[m] : sx[m];
+                    if constexpr (V == VAR_INT8) store_rowwise_i32acc(y, idx, sum[e], sxm, sw[n], mode);
+                    else if constexpr (V == VAR_FP8_ROW) store_f32(y, idx, sum[e] * (sxm * bf16_lo(sw[n])), mode);
                     else store_f32(y, idx, sum[e], mode);
                 }
             }
@@ -304,13 +402,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     }
 }
 
-template <int V, int MT, int RT, bool SG = false>
+template <int V, int MT, int RT, bool SG = false, bool FU = false>
 void launch_mt(int nw, dim3 grid, hipStream_t st, const uint8_t* qx, const float* sx, const SegmentArgs& sa,
-               int M, int K, int mode) {
+               int M, int K, int mode, const uint16_t* xbf = nullptr, uint8_t* qx_out = nullptr,
+               float* sx_out = nullptr) {
+    const size_t dyn = FU ? small_fused_lds_bytes(M, K) : 0;
     if (nw >= 8)
-        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 8, RT, SG>), grid, dim3(8 * 64), 0, st, qx, sx, sa, M, K, mode);
+        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 8, RT, SG, FU>), grid, dim3(8 * 64), dyn, st, qx, sx, sa, M, K,
+                           mode, xbf, qx_out, sx_out);
     else
-        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 4, RT, SG>), grid, dim3(4 * 64), 0, st, qx, sx, sa, M, K, mode);
+        hipLaunchKernelGGL((gemm_small_kernel<V, MT, 4, RT, SG, FU>), grid, dim3(4 * 64), dyn, st, qx, sx, sa, M, K,
+                           mode, xbf, qx_out, sx_out);
 }
 
 int64_t small_tiles(const SegmentArgs& sa, int rows) {
@@ -377,6 +479,33 @@ hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, co
     else if (variant == VAR_FP8_ROW) QLIN_SMALL(VAR_FP8_ROW);
     else QLIN_SMALL(VAR_FP8_BLOCK);
 #undef QLIN_SMALL
+    return hipGetLastError();
+}
+
+// Longer rows (the down projections) measured slower rounded inside every
+// workgroup than with the quantizer launch before the kernel.
+bool small_fused_fits(int64_t M, int64_t K) {
+    return M >= 1 && M <= kSmallFusedMaxM && K <= kSmallFusedMaxK;
+}
+
+hipError_t launch_gemm_small_fused(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa,
+                                   int mode, uint8_t* qx_out, float* sx_out, hipStream_t st) {
+    if (!small_fused_fits(M, K)) return hipErrorInvalidValue;
+    // the same tiles as the staged small-M launch
+    const bool wide = small_tiles(sa, 64) >= 256;
+    const int64_t tiles = small_tiles(sa, wide ? 64 : 16);
+    dim3 grid((unsigned)tiles);
+    const int nw = small_waves_per_tile(tiles, K);
+    const int m = (int)M, k = (int)K;
+#define QLIN_SMALL_FU(VV)                                                                                      \
+    do {                                                                                                       \
+        if (wide) launch_mt<VV, 1, 4, false, true>(nw, grid, st, nullptr, nullptr, sa, m, k, mode, x, qx_out, sx_out); \
+        else launch_mt<VV, 1, 1, false, true>(nw, grid, st, nullptr, nullptr, sa, m, k, mode, x, qx_out, sx_out);      \
+    } while (0)
+    if (variant == VAR_INT8) QLIN_SMALL_FU(VAR_INT8);
+    else if (variant == VAR_FP8_ROW) QLIN_SMALL_FU(VAR_FP8_ROW);
+    else QLIN_SMALL_FU(VAR_FP8_BLOCK);
+#undef QLIN_SMALL_FU
     return hipGetLastError();
 }
 

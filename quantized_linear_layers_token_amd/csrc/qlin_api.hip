@@ -159,7 +159,8 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
     int64_t rows = 0;   // weight rows of the call (validated by check_linear below)
     if (segments != nullptr && nseg >= 1 && nseg <= QLIN_MAX_SEGMENTS)
         for (int i = 0; i < nseg; ++i) rows += segments[i].n > 0 ? segments[i].n : 0;
-    const bool fused = ((M == 1) && (K <= qlin::kDecodeMaxK)) || qlin::linear_tokens_fits(variant, M, K, rows);
+    const bool tokens = qlin::linear_tokens_fits(variant, M, K, rows);
+    const bool fused = ((M == 1) && (K <= qlin::kDecodeMaxK)) || tokens || qlin::small_fused_fits(M, K);
     bool noop = false;
     const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, q_x, s_x, fused, &noop);
     if (st != QLIN_OK || noop) return st;
@@ -180,9 +181,12 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
     if (fused && M == 1)
         return hip_status(qlin::launch_linear_decode(variant, x, K, sa, (int)out, static_cast<uint8_t*>(q_x), s_x,
                                                      stream));
-    if (fused)
+    if (tokens)
         return hip_status(qlin::launch_linear_tokens(variant, x, M, K, sa, (int)out, static_cast<uint8_t*>(q_x), s_x,
                                                      stream));
+    if (fused)
+        return hip_status(qlin::launch_gemm_small_fused(variant, x, M, K, sa, (int)out, static_cast<uint8_t*>(q_x),
+                                                        s_x, stream));
     hipError_t e;
     if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);
     else e = qlin::launch_quant_fp8(x, M, K, variant == qlin::VAR_FP8_BLOCK ? 128 : 0, static_cast<uint8_t*>(q_x),

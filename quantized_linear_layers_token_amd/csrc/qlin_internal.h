@@ -66,6 +66,23 @@ bool linear_tokens_fits(int variant, int64_t M, int64_t K, int64_t rows);
 hipError_t launch_linear_tokens(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa, int mode,
                                 uint8_t* qx, float* sx, hipStream_t st);
 
+// Fused product for up to kSmallFusedMaxM tokens of up to kSmallFusedMaxK
+// inputs on the small-M matrix-core kernel: every workgroup rounds the tokens
+// into its LDS (dynamic: kSmallFusedScaleBytes of scales, then per token K
+// rounded up to a 128-byte step + 64 bytes of codes), so no quantizer launch
+// precedes it.
+constexpr int64_t kSmallFusedMaxM = 4;
+constexpr int64_t kSmallFusedMaxK = 4096;
+constexpr int kSmallFusedChunks = (int)(kSmallFusedMaxK / 8 / 64);   // bf16 chunks per lane and token
+constexpr int kSmallFusedGroups = (int)(kSmallFusedMaxK / 128);     // 128-input groups per token
+constexpr int kSmallFusedScaleBytes = (int)kSmallFusedMaxM * kSmallFusedGroups * 4;
+inline size_t small_fused_lds_bytes(int64_t M, int64_t K) {
+    return (size_t)kSmallFusedScaleBytes + (size_t)M * (size_t)(((K + 127) & ~int64_t(127)) + 64);
+}
+bool small_fused_fits(int64_t M, int64_t K);
+hipError_t launch_gemm_small_fused(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa,
+                                   int mode, uint8_t* qx_out, float* sx_out, hipStream_t st);
+
 // Weight-only ("equivalent") numerics: bf16 activations times dequantized
 // weights, every segment of sa in one launch.  M <= 32.
 constexpr int64_t kWeightOnlyRowMaxK = 16384;   // one-token kernel keeps the bf16 row in LDS

@@ -150,7 +150,7 @@ def test_linear_validation():
     assert lin(0, x, 0, 256, segs, 3, 0, None, None, None) == Q.QLIN_OK              # M == 0
     assert lin(0, x, 1, 250, segs, 3, 0, None, None, None) == Q.QLIN_ERR_SHAPE
     assert lin(0, None, 1, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_NULL
-    assert lin(0, x, 3, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_NULL         # M > 2 needs staging
+    assert lin(0, x, 5, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_NULL         # M > 4 needs staging
     assert lin(0, x, 2, 16400, segs, 3, 0, None, None, None) == Q.QLIN_ERR_NULL       # so do 2 long tokens
     assert lin(0, x, 4, 256, segs, 3, 0, A + 0xA000000, None, None) == Q.QLIN_ERR_NULL
     assert lin(0, x + 8, 1, 256, segs, 3, 0, None, None, None) == Q.QLIN_ERR_ALIGN

@@ -1,6 +1,8 @@
 """GPU parity of the fused projection (qlin_linear: bf16 activations in) against
 the CPU oracle, for the three schemes, one to four weight segments sharing one
-input, the one-launch path (M = 1) and the staged path (M > 1 or long K)."""
+input, the one-launch paths (one token; two tokens streaming the rows; up to
+four tokens rounded inside the small-M matrix-core kernel) and the staged path
+(quantizer launch + product: more tokens or long K)."""
 import numpy as np
 import pytest
 
@@ -73,7 +75,7 @@ CASES = [
     (1, 14336, [4096]),                     # down
     (1, 12288, [4096]),                     # Qwen3 down
     (1, 1152, [256, 384, 128, 640]),        # four segments, ragged widths
-    (3, 1024, [256, 128]),                  # staged path (small M)
+    (3, 1024, [256, 128]),                  # small-M kernel rounding the tokens itself
     (40, 512, [384]),                       # staged path (tiled GEMM)
     (64, 1024, [384, 128, 640]),            # three segments in one tiled-GEMM launch
     (300, 512, [1024, 256, 256]),           # q, k, v shaped, several token tiles
@@ -155,8 +157,19 @@ def test_linear_ragged_segments_tiled(scheme):
             assert np.max(np.abs(y - ye)) <= 4e-3 * np.max(np.abs(ye))
 
 
-# two tokens: one launch (persistent workgroups round the tokens into LDS once
-# and stream the weight rows); the staging buffers are optional there
+def one_launch(scheme, M, K, rows):
+    """Whether qlin_linear runs as one launch (staging buffers optional):
+    one token with K <= 16 Ki; two tokens streaming the rows (K <= 16 Ki, at
+    most 64 MiB of weights, block FP8 rows up to 8 KiB); up to four tokens of
+    up to 4096 inputs rounded inside the small-M kernel."""
+    if M == 1:
+        return K <= 16384
+    if M == 2 and K <= 16384 and rows * K <= 64 << 20 and not (scheme == FP8B and K > 8192):
+        return True
+    return M <= 4 and K <= 4096
+
+
+# two to four tokens: one launch (the staging buffers are optional there)
 TOKEN_CASES = [
     # (M, K, segment widths)
     (2, 128, [128]),
@@ -164,21 +177,32 @@ TOKEN_CASES = [
     (2, 1152, [256, 384, 128, 640]),     # four segments, K not a multiple of 1 KiB
     (2, 4096, [4096, 1024, 1024]),       # q, k, v
     (2, 14336, [512]),                   # down-shaped rows
+    (3, 128, [128]),
+    (3, 4080, [200, 56]),                # K not a multiple of the 128-byte step
+    (3, 4112, [200, 56]),                # just past the rows rounded in the kernel: staged
+    (4, 1152, [256, 384, 128, 640]),
+    (4, 4096, [4096, 1024, 1024]),       # q, k, v
+    (4, 12288, [256]),                   # Qwen3 down-shaped rows: staged
+    (4, 14336, [384]),                   # Llama down-shaped rows: staged
 ]
 
 
 @pytest.mark.parametrize("scheme", [W8A8, FP8R, FP8B])
 @pytest.mark.parametrize("M,K,ns", TOKEN_CASES)
 def test_linear_few_tokens_one_launch(scheme, M, K, ns):
+    if scheme == FP8B and (K % 128 or any(n % 128 for n in ns)):
+        pytest.skip("block scheme needs K and N multiples of 128")
+    print(f"few tokens scheme {scheme} M={M} K={K} ns={ns}", flush=True)
     x = W.x_bf16(7700 + M + K, M, K)
+    if M > 2:
+        x[1, : K // 2] = 0                  # a token (or its first groups) all zero
     segs = make_segments(scheme, 7710 + K + M, ns, K)
     qx_ref, sx_ref = oracle_quant(scheme, x)
-    # block FP8 rows beyond 8 KiB take the staged path: there staging is required
-    one_launch = not (scheme == FP8B and K > 8192)
-    if not one_launch:
+    one = one_launch(scheme, M, K, sum(ns))
+    if not one:
         with pytest.raises(Q().QlinError):
             run_linear_opt(scheme, x, segs, BF16, False)
-    for staged in ((False, True) if one_launch else (True,)):
+    for staged in ((False, True) if one else (True,)):
         ys, qx, sx = run_linear_opt(scheme, x, segs, BF16, staged)
         if staged:
             if scheme == W8A8:
@@ -194,9 +218,8 @@ def test_linear_few_tokens_one_launch(scheme, M, K, ns):
 
 
 def test_linear_few_tokens_ragged_rows_exact():
-    # ragged widths and the int32 accumulator of every row (two tokens; three
-    # takes the staged path)
-    for M in (2,):
+    # ragged widths and the int32 accumulator of every row, two to four tokens
+    for M in (2, 3, 4):
         K = 1040
         x = W.x_bf16(7800 + M, M, K)
         segs = make_segments(W8A8, 7810 + M, [200, 72, 1, 33], K)
@@ -226,16 +249,24 @@ def run_linear_opt(scheme, x, segs, out, staged):
     return res, (None if qx is None else host(qx)), (None if sx is None else host(sx))
 
 
-def test_linear_two_tokens_large_call_takes_staged_path():
-    # more than 64 MiB of weights at two tokens (the gate/up pair): quantizer +
-    # matrix-core kernel, so the staging buffers are required
+def test_linear_two_tokens_large_call_one_launch():
+    # more than 64 MiB of weights at two tokens (the gate/up pair): the small-M
+    # kernel rounds the tokens itself, so the staging buffers stay optional
     M, K, ns = 2, 4096, [14336, 14336]
     x = W.x_bf16(7900, M, K)
     segs = make_segments(W8A8, 7910, ns, K)
+    qx_ref, sx_ref = O.quant_act_int8(x)
+    for staged in (False, True):
+        ys, qx, _ = run_linear_opt(W8A8, x, segs, BF16, staged)
+        if staged:
+            assert np.array_equal(qx.view(np.int8), qx_ref)
+        for (qw, sw), y in zip(segs, ys):
+            assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
+
+
+def test_linear_five_tokens_need_staging():
+    M, K = 5, 1024
+    x = W.x_bf16(7950, M, K)
+    segs = make_segments(W8A8, 7960, [256], K)
     with pytest.raises(Q().QlinError):
         run_linear_opt(W8A8, x, segs, BF16, False)
-    ys, qx, _ = run_linear_opt(W8A8, x, segs, BF16, True)
-    qx_ref, sx_ref = O.quant_act_int8(x)
-    assert np.array_equal(qx.view(np.int8), qx_ref)
-    for (qw, sw), y in zip(segs, ys):
-        assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
