@@ -254,9 +254,11 @@ qlin_status qlin_linear_weight_only(qlin_scheme scheme, const uint16_t* x, int64
  *   h: bf16 [M, I], 16-byte aligned, written.
  * Same validation, q_x / s_x staging and dispatch as qlin_linear with the two
  * weights as segments: M == 1 with K <= 16384 is one launch in which each
- * wavefront streams a gate row and the up row with the same index; otherwise a
- * quantizer launch, then one product launch whose tiles hold gate rows and the
- * matching up rows.  Neither g nor u is written to memory.  h may not overlap
+ * wavefront streams a gate row and the up row with the same index; 2 <= M <= 4
+ * with K <= 4096 is one launch of the small-M kernel rounding the tokens in
+ * every workgroup (in both cases q_x / s_x are optional); otherwise a
+ * quantizer launch, then one product launch.  The product tiles hold gate rows
+ * and the matching up rows.  Neither g nor u is written to memory.  h may not overlap
  * x, q_x, s_x or either weight or scale array (QLIN_ERR_ALIAS). */
 qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
                                const void* gate_q_w, const uint16_t* gate_s_w,

@@ -26,7 +26,8 @@
 //               weight scales, per-128-input activation scales).
 //   split-K   = the NW partial tiles are summed through LDS, then the scale
 //               epilogue writes y.
-//   fused     = (FU, at most 4 tokens of at most 4096 inputs) the kernel takes
+//   fused     = (FU, at most 4 tokens of at most 4096 inputs; with or without
+//               SwiGLU) the kernel takes
 //               the bf16 activations: each of the first M wavefronts rounds
 //               one token (the standalone quantizers' arithmetic) into the
 //               workgroup's LDS while the first weight batch is in flight,
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode,
     const uint16_t* __restrict__ xbf, uint8_t* __restrict__ qx_out, float* __restrict__ sx_out) {
     typedef typename SmallAcc<V>::T Acc;
-    static_assert(!FU || (MT == 1 && !SG), "fused rounding: one token tile, no SwiGLU");
+    static_assert(!FU || MT == 1, "fused rounding: one token tile");
     // per-wave transpose buffer for one K step (RT weight tiles + MT token
     // tiles, 16 rows x 128 bytes each), reused for the split-K reduction
     constexpr int TPB = (RT + (FU ? 0 : MT)) * 2048;
@@ -362,12 +363,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                     const int n = n0 + 16 * r + (l >> 4) * 4 + e;
                     if (n < N) {
                         float gv, uv;
+                        const float sxm = FU ? fsc[m] : sx[m];
                         if constexpr (V == VAR_INT8) {
-                            gv = (float)g[e] * (sx[m] * bf16_lo(sw[n]));
-                            uv = (float)u[e] * (sx[m] * bf16_lo(sa.sw[1][n]));
+                            gv = (float)g[e] * (sxm * bf16_lo(sw[n]));
+                            uv = (float)u[e] * (sxm * bf16_lo(sa.sw[1][n]));
                         } else if constexpr (V == VAR_FP8_ROW) {
-                            gv = g[e] * (sx[m] * bf16_lo(sw[n]));
-                            uv = u[e] * (sx[m] * bf16_lo(sa.sw[1][n]));
+                            gv = g[e] * (sxm * bf16_lo(sw[n]));
+                            uv = u[e] * (sxm * bf16_lo(sa.sw[1][n]));
                         } else {
                             gv = g[e];
                             uv = u[e];
@@ -491,12 +493,29 @@ bool small_fused_fits(int64_t M, int64_t K) {
 hipError_t launch_gemm_small_fused(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa,
                                    int mode, uint8_t* qx_out, float* sx_out, hipStream_t st) {
     if (!small_fused_fits(M, K)) return hipErrorInvalidValue;
+    const int m = (int)M, k = (int)K;
+    if (mode == OUT_SWIGLU) {
+        // the same tiles as the staged SwiGLU launch
+        const int64_t I = sa.start[1];
+        const bool wide = (I + 31) / 32 >= 256;
+        dim3 grid((unsigned)((I + (wide ? 31 : 15)) / (wide ? 32 : 16)));
+        const int nw = small_waves_per_tile(grid.x, K);
+#define QLIN_SMALL_FU_SG(VV)                                                                                      \
+        do {                                                                                                      \
+            if (wide) launch_mt<VV, 1, 4, true, true>(nw, grid, st, nullptr, nullptr, sa, m, k, mode, x, qx_out, sx_out); \
+            else launch_mt<VV, 1, 2, true, true>(nw, grid, st, nullptr, nullptr, sa, m, k, mode, x, qx_out, sx_out);      \
+        } while (0)
+        if (variant == VAR_INT8) QLIN_SMALL_FU_SG(VAR_INT8);
+        else if (variant == VAR_FP8_ROW) QLIN_SMALL_FU_SG(VAR_FP8_ROW);
+        else QLIN_SMALL_FU_SG(VAR_FP8_BLOCK);
+#undef QLIN_SMALL_FU_SG
+        return hipGetLastError();
+    }
     // the same tiles as the staged small-M launch
     const bool wide = small_tiles(sa, 64) >= 256;
     const int64_t tiles = small_tiles(sa, wide ? 64 : 16);
     dim3 grid((unsigned)tiles);
     const int nw = small_waves_per_tile(tiles, K);
-    const int m = (int)M, k = (int)K;
 #define QLIN_SMALL_FU(VV)                                                                                      \
     do {                                                                                                       \
         if (wide) launch_mt<VV, 1, 4, false, true>(nw, grid, st, nullptr, nullptr, sa, m, k, mode, x, qx_out, sx_out); \

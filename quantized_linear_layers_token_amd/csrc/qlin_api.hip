@@ -236,7 +236,8 @@ qlin_status qlin_linear_weight_only(qlin_scheme scheme, const uint16_t* x, int64
 qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const void* gate_q_w,
                                const uint16_t* gate_s_w, const void* up_q_w, const uint16_t* up_s_w, int64_t I,
                                uint16_t* h, void* q_x, float* s_x, hipStream_t stream) {
-    const bool fused = (M == 1) && (K <= qlin::kDecodeMaxK);
+    const bool decode = (M == 1) && (K <= qlin::kDecodeMaxK);
+    const bool fused = decode || qlin::small_fused_fits(M, K);
     // the gate and up projections each checked as a bf16 projection into h:
     // together this covers h against x, the staging buffers and both weights
     const qlin_segment gate{gate_q_w, gate_s_w, h, I}, up{up_q_w, up_s_w, h, I};
@@ -258,8 +259,11 @@ qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M,
     for (int i = 2; i <= qlin::kMaxSegments; ++i) sa.start[i] = (int)(2 * I);
     sa.nseg = 2;
     const int mode = qlin::OUT_SWIGLU;
-    if (fused)
+    if (decode)
         return hip_status(qlin::launch_linear_decode(variant, x, K, sa, mode, static_cast<uint8_t*>(q_x), s_x, stream));
+    if (fused)
+        return hip_status(qlin::launch_gemm_small_fused(variant, x, M, K, sa, mode, static_cast<uint8_t*>(q_x), s_x,
+                                                        stream));
     hipError_t e;
     if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);
     else e = qlin::launch_quant_fp8(x, M, K, variant == qlin::VAR_FP8_BLOCK ? 128 : 0, static_cast<uint8_t*>(q_x),

@@ -196,7 +196,7 @@ def test_linear_swiglu_validation():
     assert sg(0, x, 1, 256, None, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL
     assert sg(0, x, 1, 256, gq, gs, None, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL
     assert sg(0, x, 1, 256, gq, gs, uq, us, 128, None, None, None, None) == Q.QLIN_ERR_NULL
-    assert sg(0, x, 4, 256, gq, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL  # M > 1 needs staging
+    assert sg(0, x, 5, 256, gq, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL  # M > 4 needs staging
     assert sg(0, x, 1, 256, gq, gs, uq, us, 128, h + 8, None, None, None) == Q.QLIN_ERR_ALIGN
     assert sg(0, x, 1, 256, gq, gs, uq + 8, us, 128, h, None, None, None) == Q.QLIN_ERR_ALIGN
     assert sg(0, x, 1, 256, gq, gs, uq, us, 128, uq + 256, None, None, None) == Q.QLIN_ERR_ALIAS  # h in up

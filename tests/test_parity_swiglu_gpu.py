@@ -1,7 +1,8 @@
 """GPU parity of the gate/up pair with SwiGLU applied on the way out
 (qlin_linear_swiglu) against the CPU oracle: the one-launch path (M = 1), the
-small-M matrix-core kernel (2..32 tokens, or K past the one-launch limit) and
-the tiled GEMM (more than 32 tokens), for the three schemes.
+small-M matrix-core kernel (2..32 tokens, or K past the one-launch limit; up to
+4 tokens of up to 4096 inputs rounded inside it) and the tiled GEMM (more than
+32 tokens), for the three schemes.
 
 Bound.  g and u on the device are the projections under their own tolerance
 (|dg| <= TOL max|g_ref|, likewise u; the projection tests hold them to it).
@@ -48,7 +49,7 @@ def run(scheme, x, gate, up, staged):
     I = gate[0].shape[0]
     h = empty(torch, (M * I * 2 + 64,), torch.uint8, fill=0xFF)
     qx = sx = None
-    if staged or M > 1 or K > 16384:
+    if staged or not (M == 1 and K <= 16384 or M <= 4 and K <= 4096):   # staging required
         qx = empty(torch, (M, K), torch.uint8, fill=0x55)
         sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32, fill=0x55)
     Q().qlin_linear_swiglu(scheme, dev(x), (dev(gate[0]), dev(gate[1])), (dev(up[0]), dev(up[1])), h,
@@ -92,6 +93,8 @@ CASES = [
     (1, 14336, 128),
     (1, 16512, 128),       # K past the one-launch limit: small-M kernel at M = 1
     (2, 1024, 256),
+    (4, 4096, 8192),       # rounded in the kernel, wide tiles
+    (3, 4112, 256),        # just past the in-kernel rounding: staged
     (5, 4096, 384),
     (17, 1152, 256),       # two token tiles
     (3, 512, 8192),        # wide small-M tiles (32 gate + 32 up rows)
@@ -106,8 +109,8 @@ CASES = [
 @pytest.mark.parametrize("scheme", [W8A8, FP8R, FP8B])
 @pytest.mark.parametrize("M,K,I", CASES)
 def test_swiglu_matches_oracle(scheme, M, K, I):
-    if scheme == FP8B and I % 128:
-        pytest.skip("block scheme needs I % 128 == 0")
+    if scheme == FP8B and (I % 128 or K % 128):
+        pytest.skip("block scheme needs I % 128 == 0 and K % 128 == 0")
     print(f"swiglu {NAME[scheme]} M={M} K={K} I={I}", flush=True)
     x = W.x_bf16(9000 + M + K, M, K)
     gate, up = make_pair(scheme, 9100 + I + K, I, K)
@@ -158,9 +161,11 @@ def test_swiglu_validation():
     gq, gs = dev(W.w_int8(9501, I, K)), dev(W.scale_bf16(9502, I))
     uq, us = dev(W.w_int8(9503, I, K)), dev(W.scale_bf16(9504, I))
     h = empty(torch, (2, I), torch.int16)
-    with pytest.raises(q.QlinError) as e:          # M > 1 needs the staging buffers
-        q.qlin_linear_swiglu(W8A8, x, (gq, gs), (uq, us), h)
+    x5, h5 = dev(W.x_bf16(9505, 5, K)), empty(torch, (5, I), torch.int16)
+    with pytest.raises(q.QlinError) as e:          # more than 4 tokens need the staging buffers
+        q.qlin_linear_swiglu(W8A8, x5, (gq, gs), (uq, us), h5)
     assert e.value.status == q.QLIN_ERR_NULL
+    q.qlin_linear_swiglu(W8A8, x, (gq, gs), (uq, us), h)   # two tokens: one launch, staging optional
     qx = empty(torch, (2, K), torch.uint8)
     sx = empty(torch, (2,), torch.float32)
     with pytest.raises(q.QlinError) as e:          # h over the gate weights
