@@ -1,0 +1,100 @@
+"""Inputs outside the value contract: non-finite activations (NaN, +-Inf) and
+tokens so small that Q / absmax overflows f32.  The contract leaves the
+affected token's codes and outputs unspecified; what is required is that every
+call returns, writes nothing outside its outputs (guard bands), and that the
+other tokens' results are unaffected (rounding is per token, or per 128-input
+group)."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_helpers import assert_within_tol, dev, e4m3_equal_mod_zero, empty, host, torch_mod
+
+pytestmark = pytest.mark.gpu
+W8A8, FP8R, FP8B = 0, 1, 2
+NAME = {W8A8: "int8", FP8R: "fp8_rowwise", FP8B: "fp8_block"}
+
+
+def Q():
+    import quantized_linear_layers_token_amd as q
+    return q
+
+
+def poisoned_x(seed, M, K):
+    """Token 0: NaN, +Inf, -Inf and bf16 subnormals among normal values; token 1
+    (if any): only subnormals (Q / absmax overflows f32); the rest normal."""
+    x = W.x_bf16(seed, M, K)
+    x[0, 3] = 0x7FC0                     # NaN
+    x[0, 130] = 0x7F80                   # +Inf
+    x[0, K - 1] = 0xFF80                 # -Inf
+    x[0, 7] = 0x0001                     # smallest subnormal
+    if M > 2:
+        x[1, :] = 0x0001
+        x[1, ::3] = 0x8003
+    return x
+
+
+def clean_rows(M):
+    return np.arange(2 if M > 2 else 1, M)
+
+
+def quant_ref(scheme, x):
+    if scheme == W8A8:
+        return O.quant_act_int8(x)
+    return O.quant_act_fp8(x, 128 if scheme == FP8B else 0)
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R, FP8B])
+@pytest.mark.parametrize("M,K", [(1, 4096), (3, 1024), (4, 4096), (2, 1152 * 2), (40, 512), (5, 14336)])
+def test_linear_nonfinite_tokens(scheme, M, K):
+    torch = torch_mod()
+    print(f"edges {NAME[scheme]} M={M} K={K}", flush=True)
+    x = poisoned_x(8100 + M + K, M, K)
+    N = 256
+    qw = W.w_int8(8200 + K, N, K) if scheme == W8A8 else W.w_e4m3(8200 + K, N, K)
+    sw = W.scale_bf16(8201 + K, (N // 128, K // 128) if scheme == FP8B else (N,))
+    y = empty(torch, (M * N * 2 + 64,), torch.uint8, fill=0xFF)
+    qx = empty(torch, (M * K + 64,), torch.uint8, fill=0xA5)
+    sxn = M * (K // 128) if scheme == FP8B else M
+    sx = empty(torch, (sxn + 16,), torch.float32, fill=0x5A)
+    Q().qlin_linear(scheme, dev(x), [(dev(qw), dev(sw), y[:M * N * 2].view(torch.int16).view(M, N))],
+                    q_x=qx[:M * K].view(M, K), s_x=sx[:sxn])
+    ry, rq, rs = host(y), host(qx), host(sx)
+    assert (ry[M * N * 2:] == 0xFF).all() and (rq[M * K:] == 0xA5).all(), "guard band overwritten"
+    assert (rs[sxn:].view(np.uint8) == 0x5A).all(), "scale guard band overwritten"
+    rows = clean_rows(M)
+    if len(rows):
+        q_ref, s_ref = quant_ref(scheme, x[rows])
+        codes = rq[:M * K].reshape(M, K)[rows]
+        if scheme == W8A8:
+            assert np.array_equal(codes.view(np.int8), q_ref)
+        else:
+            assert e4m3_equal_mod_zero(codes, q_ref)
+        got_s = rs[:sxn].reshape(M, -1)[rows]
+        assert np.array_equal(got_s.reshape(s_ref.shape).view(np.uint32), s_ref.view(np.uint32))
+        yb = ry[:M * N * 2].view(np.uint16).reshape(M, N)[rows]
+        if scheme == W8A8:
+            ye = O.rescale_rowwise(O.contract_int8(q_ref, qw), s_ref, sw)
+        elif scheme == FP8R:
+            ye = O.rescale_rowwise(O.contract_e4m3(q_ref, qw), s_ref, sw)
+        else:
+            ye = O.rescale_block(O.contract_e4m3_blocks(q_ref, qw), s_ref, sw)
+        assert_within_tol(yb, ye, f"clean tokens, {NAME[scheme]} M={M} K={K}")
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (4, 4096), (33, 1024)])
+def test_weight_only_nonfinite_tokens(M, K):
+    torch = torch_mod()
+    x = poisoned_x(8300 + M, M, K)
+    N = 128
+    qw = W.w_int8(8301, N, K)
+    sw = W.scale_bf16(8302, N)
+    y = empty(torch, (M * N * 2 + 64,), torch.uint8, fill=0xFF)
+    if M > 32:
+        with pytest.raises(Q().QlinError):     # weight-only numerics: at most 32 tokens
+            Q().qlin_linear_weight_only(W8A8, dev(x), [(dev(qw), dev(sw), y[:M * N * 2].view(torch.int16).view(M, N))])
+        return
+    Q().qlin_linear_weight_only(W8A8, dev(x), [(dev(qw), dev(sw), y[:M * N * 2].view(torch.int16).view(M, N))])
+    ry = host(y)
+    assert (ry[M * N * 2:] == 0xFF).all(), "guard band overwritten"
