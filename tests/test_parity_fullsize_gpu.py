@@ -100,7 +100,7 @@ def run_layer(scheme, shapes, M, seed, n_rows=48, n_cols=256):
     return checked
 
 
-def test_config1_single_projection_full():
+def test_single_projection_m16_full():
     # one W8A8 projection, M = 16, N = K = 4096, every output checked
     torch = torch_mod()
     M, N, K = 16, 4096, 4096
@@ -113,7 +113,7 @@ def test_config1_single_projection_full():
     yb = host(y).view(np.uint16)
     y_bits, y_exact, q_ref, s_ref, acc = O.linear_w8a8(x, qw, sw)
     assert np.array_equal(host(qx).view(np.int8), q_ref) and np.array_equal(host(sx), s_ref)
-    assert_within_tol(yb, y_exact, "config 1")
+    assert_within_tol(yb, y_exact, "one W8A8 projection M=16 N=K=4096")
     assert np.array_equal(yb, O.epilogue_f32_order(acc, s_ref, sw))
     # the raw int32 accumulator of the same product
     yi = empty(torch, (M, N), torch.int32)
