@@ -270,3 +270,17 @@ def test_linear_five_tokens_need_staging():
     segs = make_segments(W8A8, 7960, [256], K)
     with pytest.raises(Q().QlinError):
         run_linear_opt(W8A8, x, segs, BF16, False)
+
+
+@pytest.mark.parametrize("scheme", [FP8R, FP8B])
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_linear_few_tokens_f32_out(scheme, M):
+    # f32 outputs of the one-launch forms (scales taken from the kernel's own rounding)
+    K, ns = 1024, [256, 128]
+    x = W.x_bf16(8050 + M, M, K)
+    segs = make_segments(scheme, 8060 + M, ns, K)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
+    ys, _, _ = run_linear_opt(scheme, x, segs, F32, False)
+    for (qw, sw), y in zip(segs, ys):
+        ye = exact(scheme, qx_ref, sx_ref, qw, sw)
+        assert np.max(np.abs(y - ye)) <= 4e-3 * np.max(np.abs(ye)), f"f32, scheme {scheme}, M={M}"
