@@ -89,7 +89,10 @@ typedef enum qlin_path {
     /* the same tiles with 8 wavefronts: two groups of four split the K stages
      * of one tile and add their partial sums before the epilogue */
     QLIN_PATH_LARGE_128X128_K2 = 8,
-    QLIN_PATH_LARGE_128X64_K2 = 9
+    QLIN_PATH_LARGE_128X64_K2 = 9,
+    /* 256 x 256 with 8 wavefronts of 128 x 64, one workgroup per CU; int8 and
+     * FP8 rowwise only (QLIN_ERR_UNSUPPORTED for block FP8) */
+    QLIN_PATH_LARGE_256X256_W8 = 10
 } qlin_path;
 
 /* ---------------------------------------------------------------------- */

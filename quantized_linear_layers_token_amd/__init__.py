@@ -22,6 +22,7 @@ PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_LARGE = 0, 1, 2, 3
 # the tiled GEMM with a fixed output tile (weight rows x tokens)
 PATH_LARGE_256X128, PATH_LARGE_128X128, PATH_LARGE_128X64, PATH_LARGE_128X256 = 4, 5, 6, 7
 PATH_LARGE_128X128_K2, PATH_LARGE_128X64_K2 = 8, 9
+PATH_LARGE_256X256_W8 = 10   # int8 and FP8 rowwise only
 ABI_VERSION = 1
 MAX_K = 131072
 

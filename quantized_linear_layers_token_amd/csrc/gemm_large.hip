@@ -3,12 +3,12 @@
 // accumulation; Qwen3 8B FP8 card, "Loading": block-scaled FP8 product).
 //
 // Tiled GEMM, both operands K-contiguous.  Output tile = BN weight rows x BM
-// tokens, 256 threads = 4 wavefronts in a WN x WM grid; a wave owns a
-// (BN/WN) x (BM/WM) sub-tile of 32 x 32 MFMA tiles:
-//   int8: v_mfma_i32_32x32x32_i8      (4 per 128-byte K stage)
-//   E4M3: v_mfma_f32_32x32x64_f8f6f4  (2 per 128-byte K stage)
-// (the 16x16 int8 MFMA runs at about half the 32x32 rate on gfx950, and large
-// wave tiles keep the LDS operand reads under the ~128 B/clk LDS port).
+// tokens, 4 wavefronts (8 for the 256 x 256 tile) in a WN x WM grid; a wave
+// owns a (BN/WN) x (BM/WM) sub-tile of 32 x 32 MFMA tiles:
+//   int8: v_mfma_i32_32x32x32_i8      (4 per 128-byte K stage, 32 cycles each)
+//   E4M3: v_mfma_f32_32x32x64_f8f6f4  (2 per 128-byte K stage, 64 cycles each)
+// (32 x 32 tiles need half the LDS operand bytes per MAC of 16 x 16 ones, and
+// large wave tiles keep the operand reads under the ~128 B/clk LDS port).
 //
 // K advances in 128-byte stages.  Pipeline: stage s is loaded from global
 // memory into one of two register sets at iteration s - 2, written to one of
@@ -30,6 +30,11 @@
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8; tile ids are
 // assigned so that tiles sharing a weight panel are consecutive on one XCD.
 //
+// 256 x 256 tile (rowwise schemes): 8 wavefronts of 128 x 64, one workgroup
+// per CU (two wavefronts per SIMD).  It fetches half the bytes per MAC of a
+// 128 x 128 tile; with 128 accumulators per wavefront its operands are read
+// right before their MFMAs instead of one sub-step ahead.
+//
 // K groups (KG = 2): 512 threads in two groups of four wavefronts; group g
 // multiplies stages g, g + 2, ... of the same tile from its own pair of LDS
 // buffers, and group 1 adds its partial sums into group 0's through LDS before
@@ -49,7 +54,6 @@ namespace qlin {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBK = 128;
 
 template <int V> struct LargeAcc { typedef v16i T; };
@@ -61,27 +65,31 @@ template <int U> using IC = std::integral_constant<int, U>;
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int V, int BN, int BM, int WN, int WM, bool SG, int KG>
-__global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
+__global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa,
     int M, int K, int mode, int tiles_m, int tiles_n) {
     typedef typename LargeAcc<V>::T Acc;
-    static_assert(WN * WM == 4, "four wavefronts per K group");
+    static_assert(WN * WM == 4 || WN * WM == 8, "four or eight wavefronts per K group");
+    constexpr int GT = 64 * WN * WM;                     // threads per K group
     static_assert(KG == 1 || KG == 2, "one or two K groups");
-    constexpr int NTH = kThreads * KG;
+    constexpr int NTH = GT * KG;
     constexpr int SN = BN / WN, SM = BM / WM;              // wave sub-tile
     constexpr int TN = SN / 32, TM = SM / 32;              // 32x32 MFMA tiles per wave
     constexpr int ROWS = BN + BM;                          // LDS rows per stage (weights first)
     constexpr int STAGE = ROWS * kBK;
-    constexpr int CH = ROWS * 8 / kThreads;                // 16-byte chunks per thread per stage
-    static_assert(ROWS * 8 % kThreads == 0 && TN >= 1 && TM >= 1 && SN % 32 == 0 && SM % 32 == 0, "tile");
+    constexpr int CH = ROWS * 8 / GT;                      // 16-byte chunks per thread per stage
+    static_assert(ROWS * 8 % GT == 0 && TN >= 1 && TM >= 1 && SN % 32 == 0 && SM % 32 == 0, "tile");
     // MFMA groups per stage at which loads are issued (see compute)
     constexpr int HOOKS = V == VAR_INT8 ? 4 * TN : (V == VAR_FP8_ROW ? 2 * TN : TN * TM);
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[KG * 2 * STAGE];
+    constexpr bool LOWREG = BN == 256 && BM == 256;        // 8 wavefronts of 128 x 64
+    // stage buffers; the bf16 epilogue tile (BM rows of BN bf16 + 16 bytes) reuses them
+    constexpr int LDSB = KG * 2 * STAGE > BM * (BN * 2 + 16) ? KG * 2 * STAGE : BM * (BN * 2 + 16);
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSB];
     __shared__ float s_w_t[BN], s_x_t[BM];                // rowwise schemes: this tile's scales
 
     const int tid = threadIdx.x;
-    const int gtid = tid & (kThreads - 1);                 // thread index inside its K group
-    const int grp = __builtin_amdgcn_readfirstlane(tid / kThreads);
+    const int gtid = tid & (GT - 1);                       // thread index inside its K group
+    const int grp = __builtin_amdgcn_readfirstlane(tid / GT);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(gtid >> 6);
     const int wn = wave / WM, wm = wave % WM;
@@ -117,10 +125,11 @@ __global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
     const int m0 = __builtin_amdgcn_readfirstlane((t % tiles_m) * BM);
 
     // ---- global -> register -> LDS assignment.  Thread tid carries logical
-    // 16-byte chunk tid % 8 of rows tid / 8 + 32 j.  Loads go through buffer
+    // 16-byte chunk tid % 8 of rows tid / 8 + RP j (RP = GT / 8 rows per pass).  Loads go through buffer
     // descriptors spanning this tile's weight rows and token rows: rows past N
     // or M lie outside the descriptor's range and read as zero.
-    constexpr int JW = BN / 32, JX = BM / 32, JR = JW > JX ? JW : JX;
+    constexpr int RP = GT / 8;
+    constexpr int JW = BN / RP, JX = BM / RP, JR = JW > JX ? JW : JX;
     static_assert(JW + JX == CH, "chunk split");
     const int cthr = gtid & 7;
     const __amdgpu_buffer_rsrc_t dw = uniform_rsrc(qw + (int64_t)n0 * K, min(PR, N - n0) * K);
@@ -128,8 +137,8 @@ __global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
     const __amdgpu_buffer_rsrc_t dx = uniform_rsrc(qx + (int64_t)m0 * K, min(BM, M - m0) * K);
     int roff[JR];                                          // byte offset of each carried row
 #pragma unroll
-    for (int j = 0; j < JR; ++j) roff[j] = ((gtid >> 3) + 32 * j) * K;
-    // LDS byte offset of carried row j: row r = tid / 8 + 32 j keeps swz(r)
+    for (int j = 0; j < JR; ++j) roff[j] = ((gtid >> 3) + RP * j) * K;
+    // LDS byte offset of carried row j: row r = tid / 8 + RP j keeps swz(r)
     const int loff0 = (gtid >> 3) * kBK + ((cthr ^ swz(gtid >> 3)) << 4);
     const int nk = (K + kBK - 1) / kBK;
     // K group g multiplies stages g, g + KG, g + 2 KG, ... from its own pair of
@@ -193,16 +202,16 @@ __global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
         if (KG > 1 && s >= nk) {
             // a K group's step past the last stage: zeros
 #pragma unroll
-            for (int j = 0; j < CH; ++j) *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = v4u{0, 0, 0, 0};
+            for (int j = 0; j < CH; ++j) *reinterpret_cast<v4u*>(base + loff0 + j * RP * kBK) = v4u{0, 0, 0, 0};
         } else if ((K & (kBK - 1)) == 0) {
             // whole stages only: a stage past the end is written but never multiplied
 #pragma unroll
-            for (int j = 0; j < CH; ++j) *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = r[j];
+            for (int j = 0; j < CH; ++j) *reinterpret_cast<v4u*>(base + loff0 + j * RP * kBK) = r[j];
         } else {
             const bool ok = s * kBK + cthr * 16 < K;       // false in the ragged last stage and past the end
 #pragma unroll
             for (int j = 0; j < CH; ++j)
-                *reinterpret_cast<v4u*>(base + loff0 + j * 32 * kBK) = ok ? r[j] : v4u{0, 0, 0, 0};
+                *reinterpret_cast<v4u*>(base + loff0 + j * RP * kBK) = ok ? r[j] : v4u{0, 0, 0, 0};
         }
         if constexpr (V == VAR_FP8_BLOCK) {
             const float(&fxs)[TM] = decltype(set)::value ? fxy : fxx;
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
     // to be in use, the compiler then takes all 256 as VGPRs, selects the
     // VGPR form of the MFMAs and spills; naming one AGPR keeps the
     // accumulators in AGPRs (128 + 128).
-    if constexpr (KG > 1) asm volatile("" ::: "a0");
+    if constexpr (GT * KG > 256) asm volatile("" ::: "a0");
     Acc acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
@@ -250,7 +259,49 @@ __global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
     auto compute = [&](auto buf, const float (&fx)[TM], const float (&fw)[TN], auto&& hk) {
         __builtin_amdgcn_s_setprio(1);
         const uint8_t* base = glds + decltype(buf)::value * STAGE;
-        if constexpr (V == VAR_INT8) {
+        auto rdq = [&](int r, int c) { return *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ swz(r)) << 4)); };
+        if constexpr (LOWREG) {
+            // 256 x 256 tiles: 128 accumulators and two staging sets leave no
+            // room for a read-ahead, so per K sub-step the token tiles are
+            // read once and each weight tile right before its MFMAs (the
+            // other wavefront on the SIMD covers the LDS latency)
+            static_assert(V != VAR_FP8_BLOCK, "rowwise schemes only");
+            constexpr int SUB = V == VAR_INT8 ? 4 : 2;      // 32- or 64-byte sub-steps
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                if constexpr (V == VAR_INT8) {
+                    const int c = 2 * sub + half;
+                    v4i bq[TM];
+#pragma unroll
+                    for (int j = 0; j < TM; ++j) bq[j] = rdq(brow0 + j * 32, c);
+#pragma unroll
+                    for (int i = 0; i < TN; ++i) {
+                        const v4i aq = rdq(arow0 + i * 32, c);
+#pragma unroll
+                        for (int j = 0; j < TM; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aq, bq[j], acc[i][j], 0, 0, 0);
+                        hk(sub * TN + i);
+                    }
+                } else {
+                    const int c0 = 4 * sub + 2 * half;
+                    v8i bq[TM];
+#pragma unroll
+                    for (int j = 0; j < TM; ++j) {
+                        const v4i lo = rdq(brow0 + j * 32, c0), hi = rdq(brow0 + j * 32, c0 + 1);
+                        bq[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    }
+#pragma unroll
+                    for (int i = 0; i < TN; ++i) {
+                        const v4i lo = rdq(arow0 + i * 32, c0), hi = rdq(arow0 + i * 32, c0 + 1);
+                        const v8i aq = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                        for (int j = 0; j < TM; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq, bq[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                        hk(sub * TN + i);
+                    }
+                }
+            }
+        } else if constexpr (V == VAR_INT8) {
             constexpr int SUB = 4;                    // 32-byte K sub-steps per stage
             v4i a[SUB][TN], bb[SUB][TM];
             auto rd = [&](int sub) {
@@ -386,7 +437,7 @@ __global__ __launch_bounds__(kThreads * KG) void gemm_large_kernel(
         // group 1 hands its partial sums to group 0 through LDS (one dword per
         // lane and accumulator element, lane-contiguous), group 0 adds them
         constexpr int NACC = TN * TM * 16;
-        static_assert(4 * NACC * 64 * 4 <= (int)sizeof(lds), "partials fit the stage buffers");
+        static_assert(WN * WM * NACC * 64 * 4 <= (int)sizeof(lds), "partials fit the stage buffers");
         uint32_t* part = reinterpret_cast<uint32_t*>(lds) + wave * NACC * 64 + lane;
         __syncthreads();                                   // both groups are done with their stages
         if (grp == 1) {
@@ -540,7 +591,7 @@ template <int V, int BN, int BM, int WN, int WM, int KG = 1>
 hipError_t launch_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K, int mode,
                        hipStream_t st) {
     const int tm = (int)((M + BM - 1) / BM);
-    dim3 block(kThreads * KG);
+    dim3 block(64 * WN * WM * KG);
     if (mode == OUT_SWIGLU) {
         const int tn = (sa.start[1] + BN / 2 - 1) / (BN / 2);
         hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, true, KG>), dim3((unsigned)(tm * tn)), block, 0, st, qx,
@@ -564,6 +615,10 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
         case kTile128x256: return launch_tile<V, 128, 256, 2, 2>(qx, sx, sa, M, K, mode, st);
         case kTile128x128K2: return launch_tile<V, 128, 128, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
         case kTile128x64K2: return launch_tile<V, 128, 64, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
+        case kTile256x256W8:
+            // block FP8 rescales partial products per stage: no registers left at this tile
+            if constexpr (V == VAR_FP8_BLOCK) return hipErrorInvalidValue;
+            else return launch_tile<V, 256, 256, 2, 4>(qx, sx, sa, M, K, mode, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -571,21 +626,28 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
 }  // namespace
 
 // Tile choice, from timings of every tile on the Llama-8B projections at 256,
-// 512 and 1024 tokens (t = number of 128 x 128 tiles, 256 CUs):
+// 512, 1024 and 2048 tokens (t = number of 128 x 128 tiles, 256 CUs):
+//   FP8 rowwise with at least 224 tiles of 256 x 256 (7 of 8 CUs busy):
+//     256 x 256 with 8 wavefronts (gate/up at 512 tokens: 76 -> 63 us);
 //   t >= 384: 128 x 128, two workgroups share a CU;
 //   192 <= t < 384: 128 x 128 with two K groups (8 wavefronts, one tile per
 //     CU, two wavefronts per SIMD);
 //   t < 192: 128 x 64 with two K groups.
+// The int8 256 x 256 tile measured no faster than 128 x 128 on any shape.
 // Block FP8 scales every stage's partial products on the vector ALUs; its
 // 128 x 128 tile with two K groups needs more registers than 8 wavefronts
 // leave (it spills), so it keeps 128 x 64, with two K groups below 192 tiles.
-// The 256-row tiles need more load bandwidth per CU than the vector memory
-// path sustains next to the LDS traffic, and lose on every shape measured.
+// The 256 x 128 tiles (4 or 8 wavefronts) lost on the Llama shapes at 512 and
+// 1024 tokens.
 int large_tile_config(int variant, int64_t M, const SegmentArgs& sa) {
-    int64_t panels = 0;
-    for (int i = 0; i < sa.nseg; ++i) panels += (sa.start[i + 1] - sa.start[i] + 127) / 128;
+    int64_t panels = 0, panels256 = 0;
+    for (int i = 0; i < sa.nseg; ++i) {
+        panels += (sa.start[i + 1] - sa.start[i] + 127) / 128;
+        panels256 += (sa.start[i + 1] - sa.start[i] + 255) / 256;
+    }
     const int64_t t = ((M + 127) / 128) * panels;
     if (variant == VAR_FP8_BLOCK) return t < 192 ? kTile128x64K2 : kTile128x64;
+    if (variant == VAR_FP8_ROW && ((M + 255) / 256) * panels256 >= 224) return kTile256x256W8;
     if (t >= 384) return kTile128x128;
     return t >= 192 ? kTile128x128K2 : kTile128x64K2;
 }

@@ -103,6 +103,7 @@ CASES = [
     (100, 1024, 200),      # ragged tiles, I % 8 != 0 stores
     (300, 512, 2048),
     (640, 128, 2560),      # 128 x 128 tiles
+    (257, 128, 14336),     # FP8 rowwise: 256 x 256 tiles, ragged second token tile
 ]
 
 
