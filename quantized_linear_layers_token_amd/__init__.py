@@ -186,7 +186,8 @@ def segments_array(segments):
 
 def qlin_linear(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=None):
     """x bf16 [M, K]; segments: list of (q_w [n, K], s_w, y [M, n]) sharing x.
-    q_x / s_x: staging for the quantized activations (optional at M == 1)."""
+    q_x / s_x: staging for the quantized activations (optional where one launch
+    does the whole call: M == 1, the two-token form, or M <= 4 with K <= 4096)."""
     M, K = _dims2(x, "x")
     for qw, _, _ in segments:
         if qw.dim() != 2 or qw.shape[1] != K:
