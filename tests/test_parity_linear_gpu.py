@@ -284,3 +284,29 @@ def test_linear_few_tokens_f32_out(scheme, M):
     for (qw, sw), y in zip(segs, ys):
         ye = exact(scheme, qx_ref, sx_ref, qw, sw)
         assert np.max(np.abs(y - ye)) <= 4e-3 * np.max(np.abs(ye)), f"f32, scheme {scheme}, M={M}"
+
+
+def test_readme_example():
+    """The Python example of the README, run as written (torch tensors in,
+    staging buffers given), checked against the oracle."""
+    torch = torch_mod()
+    import quantized_linear_layers_token_amd as Qm
+    torch.manual_seed(0)
+    x = torch.randn(16, 4096, dtype=torch.bfloat16, device="cuda")
+    qw = torch.randint(-127, 128, (4096, 4096), dtype=torch.int8, device="cuda")
+    sw = (torch.rand(4096, device="cuda") * 4e-3 + 1e-3).to(torch.bfloat16)
+    y = torch.empty(16, 4096, dtype=torch.bfloat16, device="cuda")
+    qx = torch.empty(16, 4096, dtype=torch.int8, device="cuda")
+    sx = torch.empty(16, dtype=torch.float32, device="cuda")
+    Qm.qlin_linear(Qm.SCHEME_W8A8, x, [(qw, sw, y)], q_x=qx, s_x=sx)
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    qx_ref, sx_ref = O.quant_act_int8(bits(x))
+    assert np.array_equal(host(qx), qx_ref)
+    assert np.array_equal(host(sx).view(np.uint32), sx_ref.view(np.uint32))
+    acc = O.contract_int8(qx_ref, host(qw))
+    assert np.array_equal(bits(y), O.epilogue_f32_order(acc, sx_ref, bits(sw)))
+    assert_within_tol(bits(y), exact(W8A8, qx_ref, sx_ref, host(qw), bits(sw)), "README example")
