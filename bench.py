@@ -20,7 +20,8 @@ separate per-projection GEMMs.
 `roofline` is for the dominant kernel, the fused one-row decode kernel:
 achieved = algorithmic bytes per launch / average launch duration measured with
 HIP events around a graph of the 128 launches.  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same decode workload.
+oracle on a bounded sample of the same decode workload (layers in order, passing
+over the 32 layers again until --cpu-seconds of oracle time are spent).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -341,8 +342,10 @@ def time_launcher(torch, Lr, use_graph, reps=10):
 
 def cpu_baseline(torch, W, bufs, budget_s):
     """Time the CPU oracle (as it stands) on a bounded sample of the decode
-    workload: whole layers in order, until the time budget is spent.  Also
-    returns the largest error of the GPU outputs against the oracle."""
+    workload: whole layers in order, passing over the 32 layers again until
+    the time budget is spent (host copies of a layer's operands are made once,
+    outside the timed region).  Also returns the largest error of the GPU
+    outputs against the oracle (checked on the first pass)."""
     import numpy as np
 
     import oracle as O
@@ -351,43 +354,58 @@ def cpu_baseline(torch, W, bufs, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    t_total = 0.0
-    nbytes = 0
-    nproj = 0
-    max_rel = 0.0
-    exact_order = True
-    layers_done = 0
-    for lw in bufs:
+
+    def to_host(lw):
+        groups = []
         for group in W.INPUT_GROUPS:
             x = lw["in_" + group[0]][0].cpu().numpy().view(np.uint16)
             ws = []
             for name in group:
                 qw_t, sw_t, y_t = lw[name]
                 ws.append((qw_t.cpu().numpy(), sw_t.cpu().numpy().view(np.uint16), y_t.cpu().numpy().view(np.uint16)))
-            t0 = time.perf_counter()
-            qx, sx = O.quant_act_int8(x)                       # one rounding per layer input
-            outs = []
-            for qw, sw, _ in ws:
-                acc = O.contract_int8(qx, qw)
-                outs.append((acc, O.rescale_rowwise(acc, sx, sw)))
-            t_total += time.perf_counter() - t0
-            K = x.shape[1]
-            nbytes += fused_bytes(K, [qw.shape[0] for qw, _, _ in ws])
-            for (qw, sw, yg), (acc, y_exact) in zip(ws, outs):
-                nproj += 1
-                yf = (yg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-                max_rel = max(max_rel, float(np.max(np.abs(yf - y_exact)) / np.max(np.abs(y_exact))))
-                exact_order &= bool(np.array_equal(yg, O.epilogue_f32_order(acc, sx, sw)))
-        layers_done += 1
-        if t_total >= budget_s:
-            break
+            groups.append((x, ws))
+        return groups
+
+    t_total = 0.0
+    nbytes = 0
+    nproj = 0
+    max_rel = 0.0
+    exact_order = True
+    layers_done = 0
+    host_layers = []
+    first = True
+    per_layer = sum(len(g) for g in W.INPUT_GROUPS)
+    while first or t_total < budget_s:
+        for li, lw in enumerate(bufs):
+            if li == len(host_layers):
+                host_layers.append(to_host(lw))
+            for x, ws in host_layers[li]:
+                t0 = time.perf_counter()
+                qx, sx = O.quant_act_int8(x)                       # one rounding per layer input
+                outs = []
+                for qw, sw, _ in ws:
+                    acc = O.contract_int8(qx, qw)
+                    outs.append((acc, O.rescale_rowwise(acc, sx, sw)))
+                t_total += time.perf_counter() - t0
+                nbytes += fused_bytes(x.shape[1], [qw.shape[0] for qw, _, _ in ws])
+                if first:
+                    for (qw, sw, yg), (acc, y_exact) in zip(ws, outs):
+                        nproj += 1
+                        yf = (yg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                        max_rel = max(max_rel, float(np.max(np.abs(yf - y_exact)) / np.max(np.abs(y_exact))))
+                        exact_order &= bool(np.array_equal(yg, O.epilogue_f32_order(acc, sx, sw)))
+            layers_done += 1
+            if t_total >= budget_s:
+                break
+        first = False
     return {
         "value": nbytes / t_total / 1e9,
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{layers_done} of 32 decode layers ({nproj} projections with their int8 activation "
-                  f"quantization), oracle wall time {t_total:.2f} s",
+        "sample": f"{layers_done} decode layers in order over the {len(bufs)}-layer workload ({layers_done * per_layer} "
+                  f"projections with their int8 activation quantization; outputs of the first {nproj} checked), "
+                  f"oracle wall time {t_total:.2f} s",
     }, max_rel, exact_order
 
 
