@@ -1,7 +1,7 @@
 """The library's calls captured in one HIP graph and replayed: every launch
 form of qlin_linear / qlin_linear_swiglu (one token; two tokens; four tokens
 rounded in the small-M kernel; quantizer + small-M kernel; quantizer + tiled
-GEMM) must reproduce the eager results bit for bit on every replay, with
+GEMM, including its 8-wavefront 256 x 256 tile) must reproduce the eager results bit for bit on every replay, with
 eager work (output poisoning, another library call) between the replays."""
 import numpy as np
 import pytest
@@ -37,6 +37,17 @@ def build(torch):
         sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32)
         outs += [qx, sx]
         calls.append(lambda s=scheme, x=x, segs=segs, qx=qx, sx=sx: Q().qlin_linear(s, x, segs, q_x=qx, s_x=sx))
+    # FP8 rowwise, 257 tokens over two 14336-row segments: the 256 x 256 tiles
+    x = dev(W.x_bf16(9970, 257, 128))
+    segs = []
+    for j in range(2):
+        y = empty(torch, (257, 14336), torch.int16)
+        segs.append((dev(W.w_e4m3(9971 + j, 14336, 128)), dev(W.scale_bf16(9973 + j, (14336,))), y))
+        outs.append(y)
+    qx = empty(torch, (257, 128), torch.uint8)
+    sx = empty(torch, (257,), torch.float32)
+    outs += [qx, sx]
+    calls.append(lambda x=x, segs=segs, qx=qx, sx=sx: Q().qlin_linear(FP8R, x, segs, q_x=qx, s_x=sx))
     for i, (M, K) in enumerate([(1, 4096), (4, 1024), (40, 512)]):
         x = dev(W.x_bf16(9980 + i, M, K))
         gate = (dev(W.w_int8(9985 + i, 256, K)), dev(W.scale_bf16(9988 + i, 256, 1e-4, 5e-4)))
