@@ -1,0 +1,66 @@
+"""Seeded random sweep of the products: shapes drawn across all three regimes
+(one row, up to 32 rows, the tiled GEMM) with ragged M, N and K, each run on a
+kernel path drawn from those that accept it (automatic choice, a forced
+regime, or one fixed GEMM tile), against the CPU oracle with the same bars as
+the fixed cases: int8 accumulators and bf16 epilogue bit-exact, FP8 within
+4e-3 * max|y_ref| and inside the f32 summation bound."""
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_helpers import assert_within_tol
+from test_parity_gemm_gpu import (AUTO, BF16, F32, GEMV, LARGE, SMALL, block_bound, check_int8, fp8_block_case,
+                                  fp8_row_case, int8_case, rowwise_bound, run_product)
+
+pytestmark = pytest.mark.gpu
+
+FIXED_TILES = [4, 5, 6, 7, 8, 9]
+W8_TILE = 10            # 256 x 256 with 8 wavefronts: int8 and FP8 rowwise only
+N_CASES = 30
+
+
+def draw(scheme, i):
+    """Case i of a scheme: (seed, M, N, K, path), from a generator seeded by both."""
+    rng = np.random.default_rng(20261203 + 1000 * scheme + i)
+    regime = i % 3
+    M = 1 if regime == 0 else int(rng.integers(2, 33)) if regime == 1 else int(rng.integers(33, 600))
+    if scheme == 2:
+        N = 128 * int(rng.integers(1, 6))
+        K = 128 * int(rng.integers(1, 24))
+    else:
+        N = int(rng.integers(1, 700))
+        K = 16 * int(rng.integers(1, 190))
+    paths = [AUTO, LARGE] + FIXED_TILES + ([] if scheme == 2 else [W8_TILE])
+    if M <= 32:
+        paths.append(SMALL)
+    if M == 1:
+        paths.append(GEMV)
+    return 7000 + 100 * scheme + i, M, N, K, int(rng.choice(paths))
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_sweep_int8(i):
+    seed, M, N, K, path = draw(0, i)
+    check_int8(*int8_case(seed, M, N, K), path)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_sweep_fp8_rowwise(i):
+    seed, M, N, K, path = draw(1, i)
+    qx, sx, qw, sw = fp8_row_case(seed, M, N, K)
+    y_exact = O.rescale_rowwise(O.contract_e4m3(qx, qw), sx, sw)
+    y = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, N, BF16, path)
+    assert_within_tol(y, y_exact, f"fp8 rowwise {M}x{N}x{K} path {path}")
+    yf = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, N, F32, path)
+    assert np.all(np.abs(yf - y_exact) <= rowwise_bound(qx, qw, sx, sw, path)), (M, N, K, path)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_sweep_fp8_block(i):
+    seed, M, N, K, path = draw(2, i)
+    qx, sx, qw, sw = fp8_block_case(seed, M, N, K)
+    y_exact = O.rescale_block(O.contract_e4m3_blocks(qx, qw), sx, sw)
+    y = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, N, BF16, path)
+    assert_within_tol(y, y_exact, f"fp8 block {M}x{N}x{K} path {path}")
+    yf = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, N, F32, path)
+    assert np.all(np.abs(yf - y_exact) <= block_bound(qx, qw, sx, sw, path)), (M, N, K, path)
