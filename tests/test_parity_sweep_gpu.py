@@ -1,14 +1,21 @@
-"""Seeded random sweep of the products: shapes drawn across all three regimes
-(one row, up to 32 rows, the tiled GEMM) with ragged M, N and K, each run on a
-kernel path drawn from those that accept it (automatic choice, a forced
-regime, or one fixed GEMM tile), against the CPU oracle with the same bars as
-the fixed cases: int8 accumulators and bf16 epilogue bit-exact, FP8 within
-4e-3 * max|y_ref| and inside the f32 summation bound."""
+"""Seeded random sweeps against the CPU oracle, with the same bars as the fixed
+cases (int8 accumulators, codes, scales and bf16 epilogue bit-exact; FP8
+within 4e-3 * max|y_ref| and inside the f32 summation bound):
+
+  * the products: shapes drawn across all three regimes (one row, up to 32
+    rows, the tiled GEMM) with ragged M, N and K, each run on a kernel path
+    drawn from those that accept it (automatic choice, a forced regime, or
+    one fixed GEMM tile);
+  * qlin_linear: token counts drawn around every launch-form boundary, one to
+    four ragged segments, with and without the staging buffers."""
 import numpy as np
 import pytest
 
 import oracle as O
-from gpu_helpers import assert_within_tol
+import workloads as W
+from gpu_helpers import assert_within_tol, e4m3_equal_mod_zero
+from test_parity_linear_gpu import exact as linear_exact
+from test_parity_linear_gpu import make_segments, oracle_quant, run_linear
 from test_parity_gemm_gpu import (AUTO, BF16, F32, GEMV, LARGE, SMALL, block_bound, check_int8, fp8_block_case,
                                   fp8_row_case, int8_case, rowwise_bound, run_product)
 
@@ -64,3 +71,41 @@ def test_sweep_fp8_block(i):
     assert_within_tol(y, y_exact, f"fp8 block {M}x{N}x{K} path {path}")
     yf = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, N, F32, path)
     assert np.all(np.abs(yf - y_exact) <= block_bound(qx, qw, sx, sw, path)), (M, N, K, path)
+
+
+N_LINEAR = 20
+
+
+def draw_linear(scheme, i):
+    """Case i of a scheme: (seed, M, K, segment widths, staged)."""
+    rng = np.random.default_rng(20261204 + 1000 * scheme + i)
+    M = int(rng.choice([1, 1, 2, 3, 4, int(rng.integers(5, 33)), int(rng.integers(33, 300))]))
+    nseg = int(rng.integers(1, 5))
+    if scheme == 2:
+        K = 128 * int(rng.integers(1, 40))
+        ns = [128 * int(rng.integers(1, 5)) for _ in range(nseg)]
+    else:
+        K = 16 * int(rng.integers(1, 400))
+        ns = [int(rng.integers(1, 600)) for _ in range(nseg)]
+    return 8000 + 100 * scheme + i, M, K, ns, bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("scheme", [0, 1, 2])
+@pytest.mark.parametrize("i", range(N_LINEAR))
+def test_sweep_linear(scheme, i):
+    seed, M, K, ns, staged = draw_linear(scheme, i)
+    x = W.x_bf16(seed, M, K)
+    segs = make_segments(scheme, seed + 50, ns, K)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
+    ys, qx, sx = run_linear(scheme, x, segs, BF16, staged)
+    what = f"scheme {scheme} M {M} K {K} widths {ns} staged {staged}"
+    if qx is not None:
+        if scheme == 0:
+            assert np.array_equal(qx.view(np.int8), qx_ref), what
+        else:
+            assert e4m3_equal_mod_zero(qx, qx_ref), what
+        assert np.array_equal(sx.view(np.uint32), sx_ref.view(np.uint32)), what
+    for (qw, sw), y in zip(segs, ys):
+        assert_within_tol(y, linear_exact(scheme, qx_ref, sx_ref, qw, sw), what)
+        if scheme == 0:
+            assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw)), what
