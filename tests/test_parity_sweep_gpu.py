@@ -7,7 +7,9 @@ within 4e-3 * max|y_ref| and inside the f32 summation bound):
     drawn from those that accept it (automatic choice, a forced regime, or
     one fixed GEMM tile);
   * qlin_linear: token counts drawn around every launch-form boundary, one to
-    four ragged segments, with and without the staging buffers."""
+    four ragged segments, with and without the staging buffers;
+  * qlin_linear_swiglu: the same token counts, ragged gate widths (the SwiGLU
+    tests' bound on h)."""
 import numpy as np
 import pytest
 
@@ -16,6 +18,9 @@ import workloads as W
 from gpu_helpers import assert_within_tol, e4m3_equal_mod_zero
 from test_parity_linear_gpu import exact as linear_exact
 from test_parity_linear_gpu import make_segments, oracle_quant, run_linear
+from test_parity_swiglu_gpu import check as swiglu_check
+from test_parity_swiglu_gpu import make_pair
+from test_parity_swiglu_gpu import run as run_swiglu
 from test_parity_gemm_gpu import (AUTO, BF16, F32, GEMV, LARGE, SMALL, block_bound, check_int8, fp8_block_case,
                                   fp8_row_case, int8_case, rowwise_bound, run_product)
 
@@ -109,3 +114,23 @@ def test_sweep_linear(scheme, i):
         assert_within_tol(y, linear_exact(scheme, qx_ref, sx_ref, qw, sw), what)
         if scheme == 0:
             assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw)), what
+
+
+N_SWIGLU = 12
+
+
+@pytest.mark.parametrize("scheme", [0, 1, 2])
+@pytest.mark.parametrize("i", range(N_SWIGLU))
+def test_sweep_swiglu(scheme, i):
+    rng = np.random.default_rng(20261205 + 1000 * scheme + i)
+    M = int(rng.choice([1, 2, 3, 4, int(rng.integers(5, 33)), int(rng.integers(33, 300))]))
+    if scheme == 2:
+        K, I = 128 * int(rng.integers(1, 40)), 128 * int(rng.integers(1, 8))
+    else:
+        K, I = 16 * int(rng.integers(1, 400)), int(rng.integers(1, 900))
+    staged = bool(rng.integers(0, 2))
+    seed = 8500 + 100 * scheme + i
+    x = W.x_bf16(seed, M, K)
+    gate, up = make_pair(scheme, seed + 50, I, K)
+    h_bits, _, _ = run_swiglu(scheme, x, gate, up, staged)
+    swiglu_check(scheme, x, gate, up, h_bits, f"swiglu scheme {scheme} M {M} K {K} I {I} staged {staged}")
