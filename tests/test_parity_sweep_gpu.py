@@ -9,7 +9,10 @@ within 4e-3 * max|y_ref| and inside the f32 summation bound):
   * qlin_linear: token counts drawn around every launch-form boundary, one to
     four ragged segments, with and without the staging buffers;
   * qlin_linear_swiglu: the same token counts, ragged gate widths (the SwiGLU
-    tests' bound on h)."""
+    tests' bound on h);
+  * qlin_linear_weight_only: 1..32 tokens, one to four ragged segments, K on
+    both sides of the one-token kernel's limit (bf16 within the tolerance,
+    f32 inside the summation bound)."""
 import numpy as np
 import pytest
 
@@ -21,6 +24,10 @@ from test_parity_linear_gpu import make_segments, oracle_quant, run_linear
 from test_parity_swiglu_gpu import check as swiglu_check
 from test_parity_swiglu_gpu import make_pair
 from test_parity_swiglu_gpu import run as run_swiglu
+from test_parity_weight_only_gpu import NAME as WO_NAME
+from test_parity_weight_only_gpu import f32_bound as wo_f32_bound
+from test_parity_weight_only_gpu import make_segments as wo_segments
+from test_parity_weight_only_gpu import run as run_weight_only
 from test_parity_gemm_gpu import (AUTO, BF16, F32, GEMV, LARGE, SMALL, block_bound, check_int8, fp8_block_case,
                                   fp8_row_case, int8_case, rowwise_bound, run_product)
 
@@ -134,3 +141,30 @@ def test_sweep_swiglu(scheme, i):
     gate, up = make_pair(scheme, seed + 50, I, K)
     h_bits, _, _ = run_swiglu(scheme, x, gate, up, staged)
     swiglu_check(scheme, x, gate, up, h_bits, f"swiglu scheme {scheme} M {M} K {K} I {I} staged {staged}")
+
+
+N_WEIGHT_ONLY = 12
+
+
+@pytest.mark.parametrize("scheme", [0, 1, 2])
+@pytest.mark.parametrize("i", range(N_WEIGHT_ONLY))
+def test_sweep_weight_only(scheme, i):
+    rng = np.random.default_rng(20261206 + 1000 * scheme + i)
+    M = int(rng.choice([1, 1, 2, 4, int(rng.integers(5, 33))]))
+    nseg = int(rng.integers(1, 5))
+    if scheme == 2:
+        K = 128 * int(rng.choice([int(rng.integers(1, 40)), 129]))     # 129 * 128 is past the one-token limit
+        ns = [128 * int(rng.integers(1, 4)) for _ in range(nseg)]
+    else:
+        K = 16 * int(rng.choice([int(rng.integers(1, 400)), 1025]))    # 16400 is past the one-token limit
+        ns = [int(rng.integers(1, 400)) for _ in range(nseg)]
+    seed = 8700 + 100 * scheme + i
+    x = W.x_bf16(seed, M, K)
+    segs = wo_segments(scheme, seed + 50, ns, K)
+    what = f"weight-only scheme {scheme} M {M} K {K} widths {ns}"
+    ys_bf = run_weight_only(scheme, x, segs, BF16)
+    ys_f = run_weight_only(scheme, x, segs, F32)
+    for (qw, sw), yb, yf in zip(segs, ys_bf, ys_f):
+        _, y_exact = O.linear_weight_only(x, qw, sw, WO_NAME[scheme])
+        assert_within_tol(yb, y_exact, what)
+        assert np.all(np.abs(yf.astype(np.float64) - y_exact) <= wo_f32_bound(scheme, x, qw, sw, True)), what
