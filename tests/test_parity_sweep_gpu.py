@@ -12,13 +12,20 @@ within 4e-3 * max|y_ref| and inside the f32 summation bound):
     tests' bound on h);
   * qlin_linear_weight_only: 1..32 tokens, one to four ragged segments, K on
     both sides of the one-token kernel's limit (bf16 within the tolerance,
-    f32 inside the summation bound)."""
+    f32 inside the summation bound);
+  * the activation quantizers: token counts and row lengths across every
+    per-thread chunk count and the two-pass long-row kernel, inputs scaled by
+    powers of two from the subnormal to the large end of bf16 (codes and
+    scales bit-exact; every token's or group's absmax stays above 2^-118,
+    below which 127/a or 448/a overflows f32 and the codes are unspecified)."""
 import numpy as np
 import pytest
 
 import oracle as O
 import workloads as W
 from gpu_helpers import assert_within_tol, e4m3_equal_mod_zero
+from test_parity_quant_gpu import run_fp8 as quant_fp8
+from test_parity_quant_gpu import run_int8 as quant_int8
 from test_parity_linear_gpu import exact as linear_exact
 from test_parity_linear_gpu import make_segments, oracle_quant, run_linear
 from test_parity_swiglu_gpu import check as swiglu_check
@@ -168,3 +175,30 @@ def test_sweep_weight_only(scheme, i):
         _, y_exact = O.linear_weight_only(x, qw, sw, WO_NAME[scheme])
         assert_within_tol(yb, y_exact, what)
         assert np.all(np.abs(yf.astype(np.float64) - y_exact) <= wo_f32_bound(scheme, x, qw, sw, True)), what
+
+
+N_QUANT = 16
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8_token", "fp8_group"])
+@pytest.mark.parametrize("i", range(N_QUANT))
+def test_sweep_quantizers(kind, i):
+    rng = np.random.default_rng(20261207 + 100 * ["int8", "fp8_token", "fp8_group"].index(kind) + i)
+    M = int(rng.choice([1, int(rng.integers(2, 40)), int(rng.integers(40, 600))]))
+    if kind == "fp8_group":
+        K = 128 * int(rng.integers(1, 130))
+    else:
+        K = 16 * int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 2600))]))
+    e = int(rng.integers(-110, 121))          # absmax >= ~2^-113: the reciprocal scale stays finite
+    x = O.round_to_bf16_bits(O.bf16_bits_to_f64(W.x_bf16(8900 + i, M, K)) * 2.0 ** e)
+    what = f"{kind} M {M} K {K} scale 2^{e}"
+    if kind == "int8":
+        q, sc = quant_int8(x)
+        qo, so = O.quant_act_int8(x)
+        assert np.array_equal(q, qo), what
+    else:
+        group = 128 if kind == "fp8_group" else 0
+        q, sc = quant_fp8(x, group)
+        qo, so = O.quant_act_fp8(x, group)
+        assert e4m3_equal_mod_zero(q, qo), what
+    assert np.array_equal(sc.view(np.uint32), so.view(np.uint32)), what
