@@ -23,6 +23,11 @@ Readings where the pages are silent (each is also listed in the design notes):
   OCP E4M3 value); symmetric, no zero point;
 * one correctly rounded f32 divide gives s = a/Q and one gives inv = Q/a; the
   element is then fl32(x * inv), rounded half to even and saturated to +-Q;
+* for a < 2^-64 (where Q/a may exceed the f32 range) the reciprocal is taken
+  with an unbounded exponent: x and a are first scaled by 2^64 (exactly), so
+  the element is fl32(fl32(x * 2^64) * fl32(Q / (a * 2^64))); wherever Q/a is
+  finite this equals fl32(x * inv) (power-of-two scaling commutes with f32
+  rounding), so the scaling only defines the tokens that would overflow;
 * an all-zero token (or group) gets s = 0 and codes 0;
 * the E4M3 flavour is OCP E4M3 (bias 7, max 448, codes 0x7F/0xFF are NaN, no
   infinities), rounding to nearest with ties to the even code;
@@ -154,15 +159,24 @@ def e4m3_encode(v) -> np.ndarray:
 # Dynamic activation quantizers
 # --------------------------------------------------------------------------
 
+TINY = np.float32(2.0 ** -64)      # absmax below this: operands pre-scaled by 2^64
+PRE = np.float32(2.0 ** 64)
+
+
 def _scales(a: np.ndarray, Q: float):
-    """s = fl32(a / Q), inv = fl32(Q / a), both correctly rounded f32
-    divides; a zero absmax gives s = inv = 0 (the token's codes are then 0)."""
+    """s = fl32(a / Q) and the element factors (pre, inv): pre = 2^64 and
+    inv = fl32(Q / (a * 2^64)) when a < 2^-64, else pre = 1 and inv = fl32(Q / a)
+    (correctly rounded f32 divides); a zero absmax gives s = inv = 0 (the
+    token's codes are then 0).  An element is rounded from fl32(fl32(x * pre) * inv)."""
     a = a.astype(np.float32)
     q = np.float32(Q)
+    tiny = a < TINY
+    pre = np.where(tiny, PRE, np.float32(1)).astype(np.float32)
+    ap = (a * pre).astype(np.float32)                      # exact: a power-of-two scaling
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         s = (a / q).astype(np.float32)
-        inv = np.where(a > 0, q / a, np.float32(0)).astype(np.float32)
-    return s, inv
+        inv = np.where(a > 0, q / ap, np.float32(0)).astype(np.float32)
+    return s, pre, inv
 
 
 def quant_act_int8(x_bits):
@@ -171,14 +185,16 @@ def quant_act_int8(x_bits):
     W8A8 model card, intro and section "Loading": inputs are rounded to int8
     one token (row) at a time.  For each row m:
         a = max_k |x[m, k]|,  s = fl32(a / 127),  inv = fl32(127 / a),
-        q[m, k] = clamp(rint_half_even(fl32(x[m, k] * inv)), -127, 127).
+        q[m, k] = clamp(rint_half_even(fl32(x[m, k] * inv)), -127, 127)
+    (for a < 2^-64, x and a scaled by 2^64 first: see _scales).
     Returns (q int8 [M, K], s float32 [M])."""
     x = bf16_bits_to_f32(x_bits)
     if x.ndim != 2:
         raise ValueError("x must be [M, K]")
     a = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
-    s, inv = _scales(a, Q_INT8)
-    t = (x * inv[:, None]).astype(np.float32)              # one f32 multiply, RNE
+    s, pre, inv = _scales(a, Q_INT8)
+    xp = (x * pre[:, None]).astype(np.float32)             # exact (1 or 2^64)
+    t = (xp * inv[:, None]).astype(np.float32)             # one rounding f32 multiply, RNE
     q = np.clip(np.rint(t), -Q_INT8, Q_INT8).astype(np.int8)
     return q, s
 
@@ -192,7 +208,8 @@ def quant_act_fp8(x_bits, group: int = 0):
     aligned at k = 128 g (Qwen3 8B FP8 model card, "Loading": inputs rounded to
     FP8 128 inputs at a time).
     Per token or group: a = max |x|, s = fl32(a/448), inv = fl32(448/a),
-    q = E4M3_rne(clamp(fl32(x * inv), -448, 448)).
+    q = E4M3_rne(clamp(fl32(x * inv), -448, 448)) (for a < 2^-64, x and a
+    scaled by 2^64 first: see _scales).
     Returns (q uint8 codes [M, K], s float32 [M] or [M, K/128])."""
     x = bf16_bits_to_f32(x_bits)
     if x.ndim != 2:
@@ -207,8 +224,9 @@ def quant_act_fp8(x_bits, group: int = 0):
     else:
         raise ValueError("group must be 0 or 128")
     a = np.max(np.abs(xs), axis=2) if xs.shape[2] else np.zeros(xs.shape[:2], np.float32)
-    s, inv = _scales(a, Q_E4M3)
-    t = (xs * inv[:, :, None]).astype(np.float32)
+    s, pre, inv = _scales(a, Q_E4M3)
+    xp = (xs * pre[:, :, None]).astype(np.float32)         # exact (1 or 2^64)
+    t = (xp * inv[:, :, None]).astype(np.float32)
     t = np.clip(t, -Q_E4M3, Q_E4M3).astype(np.float32)
     q = e4m3_encode(t).reshape(M, K)
     return q, (s[:, 0] if group == 0 else s)

@@ -279,6 +279,31 @@ def test_power_of_two_equivariance():
         assert np.array_equal(e0, e1) and np.array_equal(t1, (t0 * np.float32(2.0 ** j)).astype(np.float32))
 
 
+def test_tiny_tokens_codes_scale_free():
+    """The codes depend on x only through x / a, so a token scaled by a power of
+    two keeps its codes: tokens and 128-groups with absmax from 2^-133 (the
+    smallest bf16 subnormal) to 2^-60, where Q/a can overflow f32, must give the
+    codes of the same values moved to absmax ~1 (a dropped 2^64 pre-scaling
+    gives +-Q for every nonzero element there)."""
+    base = W.x_bf16(12, 6, 256)
+    f = O.bf16_bits_to_f64(base)
+    for e in (-60, -64, -90, -110, -118, -122, -126, -127):
+        xs = O.round_to_bf16_bits(f * 2.0 ** e)
+        xb = O.round_to_bf16_bits(O.bf16_bits_to_f64(xs) * 2.0 ** -e)   # exact back-scaling
+        assert np.array_equal(O.bf16_bits_to_f64(xb) * 2.0 ** e, O.bf16_bits_to_f64(xs))
+        assert np.array_equal(O.quant_act_int8(xs)[0], O.quant_act_int8(xb)[0]), e
+        assert np.array_equal(O.quant_act_fp8(xs, 0)[0], O.quant_act_fp8(xb, 0)[0]), e
+        assert np.array_equal(O.quant_act_fp8(xs, 128)[0], O.quant_act_fp8(xb, 128)[0]), e
+    # a token whose only nonzero values are the smallest bf16 subnormals (a = 2^-133)
+    x = np.zeros((1, 32), np.uint16)
+    x[0, 3], x[0, 7] = 0x0001, 0x8001
+    q, s = O.quant_act_int8(x)
+    assert q[0, 3] == 127 and q[0, 7] == -127 and np.count_nonzero(q) == 2
+    assert s[0] == np.float32(2.0 ** -133 / 127)
+    e, _ = O.quant_act_fp8(x, 0)
+    assert O.e4m3_decode(e)[0, 3] == 448 and O.e4m3_decode(e)[0, 7] == -448 and np.count_nonzero(O.e4m3_decode(e)) == 2
+
+
 def test_int8_roundtrip_bound():
     x = W.x_bf16(12, 64, 4096)
     q, s = O.quant_act_int8(x)
