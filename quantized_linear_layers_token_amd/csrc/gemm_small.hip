@@ -287,10 +287,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
 #pragma unroll
                 for (int j = 0; j < kSmallFusedChunks; ++j) {
                     const int c = lane + kWave * j;
-                    float sg, inv;
-                    scales_from_absmax<true>(row_max_u32(chunk_absmax(v[j])), sg, inv);
+                    float sg;
+                    RoundFactor rf;
+                    scales_from_absmax<true>(row_max_u32(chunk_absmax(v[j])), sg, rf);
                     if (c < nch) {
-                        const v2u q = quant8<true>(v[j], inv);
+                        const v2u q = quant8<true>(v[j], rf);
                         *reinterpret_cast<v2u*>(row + 8 * c) = q;
                         if (stage) *reinterpret_cast<v2u*>(qx_out + (int64_t)t * K + 8 * c) = q;
                         if ((lane & 15) == 0) {
@@ -303,13 +304,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                 uint32_t amax = 0;
 #pragma unroll
                 for (int j = 0; j < kSmallFusedChunks; ++j) amax = max(amax, chunk_absmax(v[j]));
-                float sc, inv;
-                scales_from_absmax<V != VAR_INT8>(wave_max_u32(amax), sc, inv);
+                float sc;
+                RoundFactor rf;
+                scales_from_absmax<V != VAR_INT8>(wave_max_u32(amax), sc, rf);
 #pragma unroll
                 for (int j = 0; j < kSmallFusedChunks; ++j) {
                     const int c = lane + kWave * j;
                     if (c < nch) {
-                        const v2u q = quant8<V != VAR_INT8>(v[j], inv);
+                        const v2u q = quant8<V != VAR_INT8>(v[j], rf);
                         *reinterpret_cast<v2u*>(row + 8 * c) = q;
                         if (stage) *reinterpret_cast<v2u*>(qx_out + (int64_t)t * K + 8 * c) = q;
                     }

@@ -118,10 +118,11 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         for (int j = 0; j < CPT; ++j) {
             const int c = tid + j * kThreads;
             const uint32_t amax = row_max_u32(chunk_absmax(xb[j]));
-            float sg, inv;
-            scales_from_absmax<true>(amax, sg, inv);
+            float sg;
+            RoundFactor rf;
+            scales_from_absmax<true>(amax, sg, rf);
             if (c < nchunks) {
-                *reinterpret_cast<v2u*>(xq + c * 8) = quant8<true>(xb[j], inv);
+                *reinterpret_cast<v2u*>(xq + c * 8) = quant8<true>(xb[j], rf);
                 if ((tid & 15) == 0) gsc[c >> 4] = sg;
             }
         }
@@ -135,13 +136,14 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         amax = red[0];
 #pragma unroll
         for (int i = 1; i < kThreads / kWave; ++i) amax = max(amax, red[i]);
-        float s, inv;
-        scales_from_absmax<FP8>(amax, s, inv);
+        float s;
+        RoundFactor rf;
+        scales_from_absmax<FP8>(amax, s, rf);
         if (tid == 0) gsc[0] = s;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const int c = tid + j * kThreads;
-            if (c < nchunks) *reinterpret_cast<v2u*>(xq + c * 8) = quant8<FP8>(xb[j], inv);
+            if (c < nchunks) *reinterpret_cast<v2u*>(xq + c * 8) = quant8<FP8>(xb[j], rf);
         }
     }
     __syncthreads();

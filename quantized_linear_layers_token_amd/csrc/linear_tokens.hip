@@ -105,10 +105,11 @@ __global__ __launch_bounds__(kThreads) void linear_tokens_kernel(
             for (int j = 0; j < CPT; ++j) {
                 const int c = tid + j * kThreads;
                 const uint32_t amax = row_max_u32(chunk_absmax(xb[t][j]));
-                float sg, inv;
-                scales_from_absmax<true>(amax, sg, inv);
+                float sg;
+                RoundFactor rf;
+                scales_from_absmax<true>(amax, sg, rf);
                 if (c < nchunks) {
-                    *reinterpret_cast<v2u*>(&xq[t][code_off(c)]) = quant8<true>(xb[t][j], inv);
+                    *reinterpret_cast<v2u*>(&xq[t][code_off(c)]) = quant8<true>(xb[t][j], rf);
                     if ((tid & 15) == 0) gsc[t][c >> 4] = sg;
                 }
             }
@@ -129,13 +130,14 @@ __global__ __launch_bounds__(kThreads) void linear_tokens_kernel(
             uint32_t amax = red[t][0];
 #pragma unroll
             for (int i = 1; i < kWaves; ++i) amax = max(amax, red[t][i]);
-            float s, inv;
-            scales_from_absmax<FP8>(amax, s, inv);
+            float s;
+            RoundFactor rf;
+            scales_from_absmax<FP8>(amax, s, rf);
             if (tid == 0) gsc[t][0] = s;
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
                 const int c = tid + j * kThreads;
-                if (c < nchunks) *reinterpret_cast<v2u*>(&xq[t][code_off(c)]) = quant8<FP8>(xb[t][j], inv);
+                if (c < nchunks) *reinterpret_cast<v2u*>(&xq[t][code_off(c)]) = quant8<FP8>(xb[t][j], rf);
             }
         }
     }

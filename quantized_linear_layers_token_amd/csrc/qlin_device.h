@@ -40,6 +40,21 @@ constexpr int kWave = 64;
 
 // Exact widening of a bf16 bit pattern (low 16 bits of b) to f32.
 __device__ __forceinline__ float bf16_lo(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Factors of the activation rounding t = fl32(fl32(x * pre) * inv) for a token
+// (or group) with absmax a (bf16 bits, sign cleared) and range Q: pre = 1,
+// inv = fl32(Q / a); for a < 2^-64, where Q / a can exceed the f32 range,
+// pre = 2^64 and inv = fl32(Q / (a * 2^64)).  Scaling by 2^64 is exact, so
+// wherever Q / a is finite both forms give the same t (the dynamic scale of
+// the W8A8 and FP8 model cards, "Loading": code = x / (a / Q), rounded).
+struct RoundFactor {
+    float pre, inv;
+};
+__device__ __forceinline__ RoundFactor round_factor(uint32_t amax_bits, float q) {
+    const float pre = amax_bits < 0x1F80u ? 0x1p64f : 1.0f;       // 0x1F80: bf16 bits of 2^-64
+    const float a = __uint_as_float(amax_bits << 16) * pre;
+    return RoundFactor{pre, amax_bits == 0 ? 0.0f : q / a};
+}
 // Widening of the high bf16 of a packed pair.
 __device__ __forceinline__ float bf16_hi(uint32_t b) { return __uint_as_float(b & 0xFFFF0000u); }
 

@@ -18,32 +18,31 @@ __device__ __forceinline__ uint32_t chunk_absmax(const v4u& v) {
 }
 
 template <bool FP8>
-__device__ __forceinline__ void scales_from_absmax(uint32_t amax_bits, float& s, float& inv) {
+__device__ __forceinline__ void scales_from_absmax(uint32_t amax_bits, float& s, RoundFactor& rf) {
     const float q = FP8 ? 448.0f : 127.0f;
-    const float a = __uint_as_float(amax_bits << 16);
-    s = a / q;
-    inv = (amax_bits == 0) ? 0.0f : q / a;
+    s = __uint_as_float(amax_bits << 16) / q;
+    rf = round_factor(amax_bits, q);
 }
 
-__device__ __forceinline__ uint32_t q4_int8(uint32_t w0, uint32_t w1, float inv) {
-    auto q = [inv](float v) {
-        float t = __builtin_rintf(v * inv);
+__device__ __forceinline__ uint32_t q4_int8(uint32_t w0, uint32_t w1, RoundFactor rf) {
+    auto q = [rf](float v) {
+        float t = __builtin_rintf((v * rf.pre) * rf.inv);
         t = fminf(fmaxf(t, -127.0f), 127.0f);
         return (uint32_t)(uint8_t)(int8_t)(int)t;
     };
     return q(bf16_lo(w0)) | (q(bf16_hi(w0)) << 8) | (q(bf16_lo(w1)) << 16) | (q(bf16_hi(w1)) << 24);
 }
 
-__device__ __forceinline__ uint32_t q4_fp8(uint32_t w0, uint32_t w1, float inv) {
-    auto c = [inv](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+__device__ __forceinline__ uint32_t q4_fp8(uint32_t w0, uint32_t w1, RoundFactor rf) {
+    auto c = [rf](float v) { return fminf(fmaxf((v * rf.pre) * rf.inv, -448.0f), 448.0f); };
     const uint32_t lo = e4m3_pack_lo(c(bf16_lo(w0)), c(bf16_hi(w0)));
     return e4m3_pack_hi(lo, c(bf16_lo(w1)), c(bf16_hi(w1)));
 }
 
 template <bool FP8>
-__device__ __forceinline__ v2u quant8(const v4u& v, float inv) {
-    if constexpr (FP8) return v2u{q4_fp8(v.x, v.y, inv), q4_fp8(v.z, v.w, inv)};
-    else return v2u{q4_int8(v.x, v.y, inv), q4_int8(v.z, v.w, inv)};
+__device__ __forceinline__ v2u quant8(const v4u& v, RoundFactor rf) {
+    if constexpr (FP8) return v2u{q4_fp8(v.x, v.y, rf), q4_fp8(v.z, v.w, rf)};
+    else return v2u{q4_int8(v.x, v.y, rf), q4_int8(v.z, v.w, rf)};
 }
 
 __device__ __forceinline__ int dot16_i8(const v4u& w, const v4u& x, int acc) {

@@ -29,42 +29,45 @@ __device__ __forceinline__ uint32_t chunk_absmax_bits(const v4u& v) {
     return max(max(m0, m1), max(m2, m3));
 }
 
-// s = fl32(a / Q), inv = fl32(Q / a) (0 for an all-zero row).  Both are IEEE
-// correctly rounded divides (the default for f32 division in HIP).
+// s = fl32(a / Q) and the rounding factors (round_factor: inv = fl32(Q / a),
+// with x and a pre-scaled by 2^64 below a = 2^-64; 0 for an all-zero row).
+// The divides are IEEE correctly rounded divides (the default for f32
+// division in HIP).
 template <bool FP8>
-__device__ __forceinline__ void token_scales(uint32_t amax_bits, float& s, float& inv) {
+__device__ __forceinline__ void token_scales(uint32_t amax_bits, float& s, RoundFactor& rf) {
     const float q = FP8 ? 448.0f : 127.0f;
-    const float a = __uint_as_float(amax_bits << 16);
-    s = a / q;
-    inv = (amax_bits == 0) ? 0.0f : q / a;
+    s = __uint_as_float(amax_bits << 16) / q;
+    rf = round_factor(amax_bits, q);
 }
 
-__device__ __forceinline__ int8_t q_int8(float x, float inv) {
-    float t = __builtin_rintf(x * inv);             // v_rndne_f32: half to even
+__device__ __forceinline__ int8_t q_int8(float x, RoundFactor rf) {
+    float t = __builtin_rintf((x * rf.pre) * rf.inv);   // v_rndne_f32: half to even
     t = fminf(fmaxf(t, -127.0f), 127.0f);
     return (int8_t)(int)t;
 }
 
-__device__ __forceinline__ float sat448(float t) { return fminf(fmaxf(t, -448.0f), 448.0f); }
+__device__ __forceinline__ float sat448(float x, RoundFactor rf) {
+    return fminf(fmaxf((x * rf.pre) * rf.inv, -448.0f), 448.0f);
+}
 
 // 8 bf16 (one 16-byte chunk) -> 8 int8 or 8 E4M3 codes (one 8-byte word).
 template <bool FP8>
-__device__ __forceinline__ v2u quant_chunk(const v4u& v, float inv) {
+__device__ __forceinline__ v2u quant_chunk(const v4u& v, RoundFactor rf) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[2];
     if constexpr (FP8) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            uint32_t lo = e4m3_pack_lo(sat448(bf16_lo(w[2 * i]) * inv), sat448(bf16_hi(w[2 * i]) * inv));
-            o[i] = e4m3_pack_hi(lo, sat448(bf16_lo(w[2 * i + 1]) * inv), sat448(bf16_hi(w[2 * i + 1]) * inv));
+            uint32_t lo = e4m3_pack_lo(sat448(bf16_lo(w[2 * i]), rf), sat448(bf16_hi(w[2 * i]), rf));
+            o[i] = e4m3_pack_hi(lo, sat448(bf16_lo(w[2 * i + 1]), rf), sat448(bf16_hi(w[2 * i + 1]), rf));
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            uint32_t b0 = (uint8_t)q_int8(bf16_lo(w[2 * i]), inv);
-            uint32_t b1 = (uint8_t)q_int8(bf16_hi(w[2 * i]), inv);
-            uint32_t b2 = (uint8_t)q_int8(bf16_lo(w[2 * i + 1]), inv);
-            uint32_t b3 = (uint8_t)q_int8(bf16_hi(w[2 * i + 1]), inv);
+            uint32_t b0 = (uint8_t)q_int8(bf16_lo(w[2 * i]), rf);
+            uint32_t b1 = (uint8_t)q_int8(bf16_hi(w[2 * i]), rf);
+            uint32_t b2 = (uint8_t)q_int8(bf16_lo(w[2 * i + 1]), rf);
+            uint32_t b3 = (uint8_t)q_int8(bf16_hi(w[2 * i + 1]), rf);
             o[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
         }
     }
@@ -95,15 +98,16 @@ __global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(
     __syncthreads();
     amax = max(max(red[0], red[1]), max(red[2], red[3]));
 
-    float sc, inv;
-    token_scales<FP8>(amax, sc, inv);
+    float sc;
+    RoundFactor rf;
+    token_scales<FP8>(amax, sc, rf);
     if (tid == 0) s[m] = sc;
 
     v2u* qr = reinterpret_cast<v2u*>(q + m * K);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + j * kQuantThreads;
-        if (c < nchunks) qr[c] = quant_chunk<FP8>(v[j], inv);
+        if (c < nchunks) qr[c] = quant_chunk<FP8>(v[j], rf);
     }
 }
 
@@ -123,11 +127,12 @@ __global__ __launch_bounds__(kQuantThreads) void quant_token_loop_kernel(
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
     __syncthreads();
     amax = max(max(red[0], red[1]), max(red[2], red[3]));
-    float sc, inv;
-    token_scales<FP8>(amax, sc, inv);
+    float sc;
+    RoundFactor rf;
+    token_scales<FP8>(amax, sc, rf);
     if (tid == 0) s[m] = sc;
     v2u* qr = reinterpret_cast<v2u*>(q + m * K);
-    for (int64_t c = tid; c < nchunks; c += kQuantThreads) qr[c] = quant_chunk<FP8>(xr[c], inv);
+    for (int64_t c = tid; c < nchunks; c += kQuantThreads) qr[c] = quant_chunk<FP8>(xr[c], rf);
 }
 
 // 128-input groups: group g of the flattened [M*K] array is x[128 g, 128 g + 128)
@@ -141,10 +146,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group128_fp8_kernel(
     const int64_t c = g * 16 + (tid & 15);    // chunk index in the flattened array
     const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x) + c);
     const uint32_t amax = row_max_u32(chunk_absmax_bits(v));
-    float sc, inv;
-    token_scales<true>(amax, sc, inv);
+    float sc;
+    RoundFactor rf;
+    token_scales<true>(amax, sc, rf);
     if ((tid & 15) == 0) s[g] = sc;
-    reinterpret_cast<v2u*>(q)[c] = quant_chunk<true>(v, inv);
+    reinterpret_cast<v2u*>(q)[c] = quant_chunk<true>(v, rf);
 }
 
 template <bool FP8>

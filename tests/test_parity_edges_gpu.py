@@ -1,8 +1,10 @@
-"""Inputs outside the value contract: non-finite activations (NaN, +-Inf) and
-tokens so small that Q / absmax overflows f32.  The contract leaves the
-affected token's codes and outputs unspecified; what is required is that every
-call returns, writes nothing outside its outputs (guard bands), and that the
-other tokens' results are unaffected (rounding is per token, or per 128-input
+"""Inputs outside the value contract, non-finite activations (NaN, +-Inf),
+next to tokens made only of bf16 subnormals (inside the contract: Q / absmax
+overflows f32 there, and the rounding pre-scales x and absmax by 2^64).  The
+contract leaves a non-finite token's codes and outputs unspecified; what is
+required is that every call returns, writes nothing outside its outputs (guard
+bands), and that every other token -- the subnormal one included -- gets the
+oracle's codes, scales and outputs (rounding is per token, or per 128-input
 group)."""
 import numpy as np
 import pytest
@@ -23,7 +25,7 @@ def Q():
 
 def poisoned_x(seed, M, K):
     """Token 0: NaN, +Inf, -Inf and bf16 subnormals among normal values; token 1
-    (if any): only subnormals (Q / absmax overflows f32); the rest normal."""
+    (if M > 2): only subnormals (Q / absmax overflows f32); the rest normal."""
     x = W.x_bf16(seed, M, K)
     x[0, 3] = 0x7FC0                     # NaN
     x[0, 130] = 0x7F80                   # +Inf
@@ -36,7 +38,8 @@ def poisoned_x(seed, M, K):
 
 
 def clean_rows(M):
-    return np.arange(2 if M > 2 else 1, M)
+    """Every token but the non-finite one."""
+    return np.arange(1, M)
 
 
 def quant_ref(scheme, x):

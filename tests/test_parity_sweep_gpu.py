@@ -16,8 +16,8 @@ within 4e-3 * max|y_ref| and inside the f32 summation bound):
   * the activation quantizers: token counts and row lengths across every
     per-thread chunk count and the two-pass long-row kernel, inputs scaled by
     powers of two from the subnormal to the large end of bf16 (codes and
-    scales bit-exact; every token's or group's absmax stays above 2^-118,
-    below which 127/a or 448/a overflows f32 and the codes are unspecified)."""
+    scales bit-exact, including tokens and groups whose absmax lies below
+    2^-118, where Q/a overflows f32 and the rounding pre-scales by 2^64)."""
 import numpy as np
 import pytest
 
@@ -189,7 +189,8 @@ def test_sweep_quantizers(kind, i):
         K = 128 * int(rng.integers(1, 130))
     else:
         K = 16 * int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 2600))]))
-    e = int(rng.integers(-110, 121))          # absmax >= ~2^-113: the reciprocal scale stays finite
+    # every fourth case with absmax below 2^-118 (Q / a overflows f32 there)
+    e = int(rng.integers(-125, -119)) if i % 4 == 0 else int(rng.integers(-118, 121))
     x = O.round_to_bf16_bits(O.bf16_bits_to_f64(W.x_bf16(8900 + i, M, K)) * 2.0 ** e)
     what = f"{kind} M {M} K {K} scale 2^{e}"
     if kind == "int8":
