@@ -103,9 +103,11 @@ typedef enum qlin_path {
  * token of the input gets its own int8 scale).  For each row m of x (bf16 [M, K]):
  *   a = max_k |x[m,k]|;  s[m] = fl32(a / 127);  inv = fl32(127 / a) (0 if a == 0)
  *   q[m,k] = clamp(round_half_even(fl32(x[m,k] * inv)), -127, 127)
- * q: int8 [M, K] (written), s: f32 [M] (written).  Non-finite inputs and rows
- * whose 127/a overflows f32 are outside the contract (no fault, values
- * unspecified). */
+ * For a < 2^-64 (where 127/a can overflow f32) x and a are first scaled by
+ * 2^64, exactly: q = ...(fl32(fl32(x * 2^64) * fl32(127 / (a * 2^64)))), which
+ * equals the form above wherever 127/a is finite.
+ * q: int8 [M, K] (written), s: f32 [M] (written).  Non-finite inputs are
+ * outside the contract (no fault, values of that row unspecified). */
 qlin_status qlin_quant_act_int8(const uint16_t* x, int64_t M, int64_t K,
                                 int8_t* q, float* s, hipStream_t stream);
 
@@ -117,7 +119,8 @@ qlin_status qlin_quant_act_int8(const uint16_t* x, int64_t M, int64_t K,
  *                 s is f32 [M, K/128] row-major.
  * Per token or group: s = fl32(a / 448), inv = fl32(448 / a) (0 if a == 0),
  *   q = nearest E4M3 code of clamp(fl32(x * inv), -448, 448), ties to even,
- *   sign of zero kept. */
+ *   sign of zero kept; for a < 2^-64 with x and a scaled by 2^64 first, as
+ *   for qlin_quant_act_int8.  Non-finite inputs: as for qlin_quant_act_int8. */
 qlin_status qlin_quant_act_fp8(const uint16_t* x, int64_t M, int64_t K, int32_t group,
                                uint8_t* q, float* s, hipStream_t stream);
 
