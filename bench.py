@@ -48,7 +48,9 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # the pages' protocol: median of 10 runs after 3 warm-ups ("Llama 3.1 8B
+    # Instruct FP8" benchmark page, section "Every number")
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--quick", action="store_true", help="headline only (no secondary sweeps, no CPU baseline)")
@@ -139,18 +141,39 @@ def capture(torch, fn, use_graph=True):
     return g.replay
 
 
-def time_events(torch, fn, reps):
-    """Milliseconds per call of fn, from HIP events on the current stream."""
+def time_runs(torch, fn, reps):
+    """Milliseconds of each of `reps` back-to-back calls of fn, from HIP events
+    recorded between the calls on the current stream (no synchronization in
+    between)."""
     st = torch.cuda.current_stream()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    a.record(st)
-    for _ in range(reps):
+    ev[0].record(st)
+    for i in range(reps):
         fn()
-    b.record(st)
-    b.synchronize()
-    return a.elapsed_time(b) / reps
+        ev[i + 1].record(st)
+    ev[-1].synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def time_events(torch, fn, reps):
+    """Median milliseconds per call of fn over `reps` timed calls (the caller
+    has run the warm-ups)."""
+    return median(time_runs(torch, fn, reps))
+
+
+def time_warm(torch, fn, reps=10, warmup=3):
+    """The pages' protocol for one measurement: `warmup` untimed calls, then
+    the median of `reps` timed calls."""
+    for _ in range(warmup):
+        fn()
+    return time_events(torch, fn, reps)
 
 
 # ---------------------------------------------------------------------------
@@ -330,22 +353,32 @@ def layer_set(torch, Q, W, scheme, shapes, M, layers, dev, seed0):
     return Lr, nbytes, ops, keep
 
 
-def time_launcher(torch, Lr, use_graph, reps=10):
-    fn = capture(torch, Lr.run, use_graph)
-    fn()
-    return time_events(torch, fn, reps)
+def time_launcher(torch, Lr, use_graph, reps=10, warmup=3):
+    return time_warm(torch, capture(torch, Lr.run, use_graph), reps, warmup)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ---------------------------------------------------------------------------
 # CPU oracle leg
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(torch, W, bufs, budget_s):
+def cpu_baseline(torch, W, bufs, budget_s, runs=3):
     """Time the CPU oracle (as it stands) on a bounded sample of the decode
-    workload: whole layers in order, passing over the 32 layers again until
-    the time budget is spent (host copies of a layer's operands are made once,
-    outside the timed region).  Also returns the largest error of the GPU
-    outputs against the oracle (checked on the first pass)."""
+    workload, `runs` times (median reported): each run takes whole layers in
+    order, passing over the 32 layers again until its share of the time budget
+    is spent (host copies of a layer's operands are made once, outside the
+    timed region).  Also returns the largest error of the GPU outputs against
+    the oracle (checked on the first pass of the first run)."""
     import numpy as np
 
     import oracle as O
@@ -366,47 +399,55 @@ def cpu_baseline(torch, W, bufs, budget_s):
             groups.append((x, ws))
         return groups
 
-    t_total = 0.0
-    nbytes = 0
-    nproj = 0
-    max_rel = 0.0
-    exact_order = True
-    layers_done = 0
     host_layers = []
-    first = True
     per_layer = sum(len(g) for g in W.INPUT_GROUPS)
-    while first or t_total < budget_s:
-        for li, lw in enumerate(bufs):
-            if li == len(host_layers):
-                host_layers.append(to_host(lw))
-            for x, ws in host_layers[li]:
-                t0 = time.perf_counter()
-                qx, sx = O.quant_act_int8(x)                       # one rounding per layer input
-                outs = []
-                for qw, sw, _ in ws:
-                    acc = O.contract_int8(qx, qw)
-                    outs.append((acc, O.rescale_rowwise(acc, sx, sw)))
-                t_total += time.perf_counter() - t0
-                nbytes += fused_bytes(x.shape[1], [qw.shape[0] for qw, _, _ in ws])
-                if first:
-                    for (qw, sw, yg), (acc, y_exact) in zip(ws, outs):
-                        nproj += 1
-                        yf = (yg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-                        max_rel = max(max_rel, float(np.max(np.abs(yf - y_exact)) / np.max(np.abs(y_exact))))
-                        exact_order &= bool(np.array_equal(yg, O.epilogue_f32_order(acc, sx, sw)))
-            layers_done += 1
-            if t_total >= budget_s:
-                break
-        first = False
+    check = {"nproj": 0, "max_rel": 0.0, "exact": True}
+
+    def one_run(budget, verify):
+        t_total = 0.0
+        nbytes = 0
+        layers_done = 0
+        first = True
+        while first or t_total < budget:
+            for li, lw in enumerate(bufs):
+                if li == len(host_layers):
+                    host_layers.append(to_host(lw))
+                for x, ws in host_layers[li]:
+                    t0 = time.perf_counter()
+                    qx, sx = O.quant_act_int8(x)                       # one rounding per layer input
+                    outs = []
+                    for qw, sw, _ in ws:
+                        acc = O.contract_int8(qx, qw)
+                        outs.append((acc, O.rescale_rowwise(acc, sx, sw)))
+                    t_total += time.perf_counter() - t0
+                    nbytes += fused_bytes(x.shape[1], [qw.shape[0] for qw, _, _ in ws])
+                    if first and verify:
+                        for (qw, sw, yg), (acc, y_exact) in zip(ws, outs):
+                            check["nproj"] += 1
+                            yf = (yg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                            check["max_rel"] = max(check["max_rel"],
+                                                   float(np.max(np.abs(yf - y_exact)) / np.max(np.abs(y_exact))))
+                            check["exact"] &= bool(np.array_equal(yg, O.epilogue_f32_order(acc, sx, sw)))
+                layers_done += 1
+                if t_total >= budget:
+                    break
+            first = False
+        return nbytes / t_total / 1e9, layers_done, t_total
+
+    results = [one_run(budget_s / runs, i == 0) for i in range(runs)]
+    rates = [r[0] for r in results]
     return {
-        "value": nbytes / t_total / 1e9,
+        "value": median(rates),
         "unit": "GB/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": f"{layers_done} decode layers in order over the {len(bufs)}-layer workload ({layers_done * per_layer} "
-                  f"projections with their int8 activation quantization; outputs of the first {nproj} checked), "
-                  f"oracle wall time {t_total:.2f} s",
-    }, max_rel, exact_order
+        "sample": f"median of {runs} runs, each whole decode layers in order over the {len(bufs)}-layer workload "
+                  f"for about {budget_s / runs:.0f} s of oracle time ({', '.join(str(r[1]) for r in results)} "
+                  f"layers of {per_layer} projections with their int8 activation quantization; GB/s "
+                  f"{', '.join(f'{r:.3f}' for r in rates)}); outputs of the first {check['nproj']} projections "
+                  f"checked",
+    }, check["max_rel"], check["exact"]
 
 
 # ---------------------------------------------------------------------------
@@ -483,17 +524,20 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} decode steps")
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_events(torch, step, args.steps)
+    runs = time_runs(torch, step, args.steps)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = median(runs)
     value = fused_step_bytes / (ms * 1e-3) / 1e9
-    log(f"decode step {ms:.4f} ms (wall {wall_ms:.4f} ms)  {value:.1f} GB/s")
+    log(f"decode step median {ms:.4f} ms, mean {sum(runs) / len(runs):.4f} ms (wall {wall_ms:.4f} ms)  "
+        f"{value:.1f} GB/s")
 
     # ---- roofline of the dominant kernel: the fused one-row projection -----
     # (the step is made of these launches only: avg launch = step time / 128)
     n_launch = len(F.calls)
-    ms_f = time_events(torch, step, max(3, args.steps // 2))
+    ms_f = ms
     avg_launch_us = ms_f * 1e3 / n_launch
     bytes_per_launch = fused_step_bytes / n_launch
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
@@ -508,21 +552,25 @@ def main():
     secondary = {}
     # the two-kernel form of the same step (quantizer + one-row product per projection)
     two = capture(torch, L.run, use_graph)
-    two()
-    ms_two = time_events(torch, two, max(3, args.steps // 2))
+    for _ in range(args.warmup):
+        two()
+    ms_two = time_events(torch, two, args.steps)
     gemv_only = capture(torch, G.run, use_graph)
-    gemv_only()
-    ms_gemv = time_events(torch, gemv_only, max(3, args.steps // 2))
+    for _ in range(args.warmup):
+        gemv_only()
+    ms_gemv = time_events(torch, gemv_only, args.steps)
     # the same step under weight-only numerics (bf16 input never rounded)
     wo = capture(torch, WO.run, use_graph)
-    wo()
-    ms_wo = time_events(torch, wo, max(3, args.steps // 2))
+    for _ in range(args.warmup):
+        wo()
+    ms_wo = time_events(torch, wo, args.steps)
     secondary["decode_weight_only"] = {"ms_per_step": round(ms_wo, 4),
                                        "gbs": round(fused_step_bytes / (ms_wo * 1e-3) / 1e9, 1)}
     # gate/up with SwiGLU in the epilogue, down reading its output
     sg = capture(torch, S.run, use_graph)
-    sg()
-    ms_sg = time_events(torch, sg, max(3, args.steps // 2))
+    for _ in range(args.warmup):
+        sg()
+    ms_sg = time_events(torch, sg, args.steps)
     secondary["decode_swiglu_chained"] = {"ms_per_step": round(ms_sg, 4), "launches": len(S.calls),
                                           "gbs": round(swiglu_step_bytes / (ms_sg * 1e-3) / 1e9, 1)}
     log(f"swiglu-chained step {ms_sg:.4f} ms {secondary['decode_swiglu_chained']}")
@@ -539,8 +587,7 @@ def main():
             for q, s, qw, sw, y, N, K in items:
                 P.gemm("qlin_gemm_w8a8", q, s, qw, sw, y, 1, N, K)
             fn = capture(torch, P.run, use_graph)
-            fn()
-            t = time_events(torch, fn, 5)
+            t = time_warm(torch, fn)
             shape_gbs[name] = round(len(items) * decode_bytes(N, K) / (t * 1e-3) / 1e9, 1)
         secondary["decode_gemv_gbs_per_shape"] = shape_gbs
         log(f"per-shape GB/s {shape_gbs}")
@@ -614,13 +661,11 @@ def main():
                 nbw += N * K + 2 * N + 2 * M * K + 2 * M * N
                 ops += 2 * M * N * K
             fn = capture(torch, P.run, use_graph)
-            fn()
-            t = time_events(torch, fn, 10)
+            t = time_warm(torch, fn)
             small[str(M)] = {"gbs": round(nb / (t * 1e-3) / 1e9, 1), "tops": round(ops / (t * 1e-3) / 1e12, 2),
                              "us_per_layer": round(t * 1e3, 2)}
             fw = capture(torch, PW.run, use_graph)
-            fw()
-            t = time_events(torch, fw, 10)
+            t = time_warm(torch, fw)
             small_wo[str(M)] = {"gbs": round(nbw / (t * 1e-3) / 1e9, 1), "us_per_layer": round(t * 1e3, 2)}
             del keep
         # (one layer's weights, 218 MB, re-read each replay: partly served by the 256 MB MALL)
@@ -640,14 +685,10 @@ def main():
                 f_prod = capture(torch, prod.run, use_graph)
                 f_fused = capture(torch, fused.run, use_graph)
                 f_sg = capture(torch, swiglu.run, use_graph)
-                f_full()
-                f_prod()
-                f_fused()
-                f_sg()
-                t_full = time_events(torch, f_full, 5)
-                t_prod = time_events(torch, f_prod, 5)
-                t_fused = time_events(torch, f_fused, 5)
-                t_sg = time_events(torch, f_sg, 5)
+                t_full = time_warm(torch, f_full)
+                t_prod = time_warm(torch, f_prod)
+                t_fused = time_warm(torch, f_fused)
+                t_sg = time_warm(torch, f_sg)
                 key = f"prefill_{variant}_M{M}"
                 secondary[key] = {
                     "tops_fused_linear": round(ops / (t_fused * 1e-3) / 1e12, 1),
@@ -679,6 +720,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_mean": round(sum(runs) / len(runs), 4),
+        "timing": f"median of {args.steps} steps after {args.warmup} warm-up steps (HIP events between steps)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -139,10 +139,18 @@ qlin_status qlin_gemv_w8a8(const int8_t* q_x, const float* s_x,
                            void* y, int64_t N, int64_t K, qlin_out out,
                            hipStream_t stream);
 
-/* W8A8 product for any M (same formula per row m; s_x f32 [M], y [M, N]).
+/* W8A8 product for any M ("Llama 3.1 8B Instruct W8A8" model card, intro:
+ * int8 weights with one bf16 scale per output row times per-token int8
+ * activations; "Loading": one row goes to a kernel reading each weight byte
+ * once, up to 32 rows to the matrix units, longer inputs to a tiled product
+ * summing the int8 products in int32).  Same formula per row m as
+ * qlin_gemv_w8a8; s_x f32 [M], y [M, N].
  * Dispatch (AUTO): M == 1 -> the one-row kernel; 2..32 -> matrix-core
  * streaming kernel; larger -> tiled matrix-core GEMM.  A fused projection
- * (e.g. q/k/v or gate/up) is the same call on row-concatenated q_w / s_w. */
+ * (e.g. q/k/v or gate/up) is the same call on row-concatenated q_w / s_w.
+ * Same validation and error behaviour as every entry point (see the top of
+ * this file); _ex forces one kernel (qlin_path), QLIN_ERR_UNSUPPORTED where it
+ * cannot run this call. */
 qlin_status qlin_gemm_w8a8(const int8_t* q_x, const float* s_x,
                            const int8_t* q_w, const uint16_t* s_w,
                            void* y, int64_t M, int64_t N, int64_t K, qlin_out out,

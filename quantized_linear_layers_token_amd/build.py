@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libqlin.so")
 ARCH = "gfx950"
 SOURCES = ["quant_act.hip", "gemv.hip", "gemm_small.hip", "gemm_large.hip", "linear.hip", "linear_tokens.hip", "weight_only.hip",
            "qlin_api.hip"]
-HEADERS = ["qlin_device.h", "qlin_internal.h", "qlin_rows.h"]
+HEADERS = ["qlin_device.h", "qlin_internal.h", "qlin_round.h", "qlin_rows.h"]
 
 # Never fast-math, never flush denormals: the quantizers are bit-exact against
 # IEEE f32 divide / multiply / round-half-even.  Packed FP32 instructions are

@@ -420,16 +420,13 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
         write(IC<0>{}, IC<0>{}, gs(kt + 2));
         __syncthreads();
     }
+    // The K-group hand-off and the epilogue read the accumulators next.  The
+    // padding sits inside each exit path: the compiler places its accumulator
+    // copies where the two paths join.
+    mfma_drain();
     if (kt < nko) {
         compute(IC<0>{}, fx0, fw0, [&](int) {});
-        // The epilogue reads the accumulators right after these MFMAs.  With the
-        // wave at raised priority, the last register of the last 32x32x64 E4M3
-        // MFMA was read before that MFMA had written it (the value lacked
-        // exactly that MFMA's contribution) although the compiler had padded
-        // the read: 64 more idle issue slots, once per tile.
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::);
-        __builtin_amdgcn_sched_barrier(0);
+        mfma_drain();
     }
     __builtin_amdgcn_s_setprio(0);
 

@@ -251,15 +251,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                         } else {
                             const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                            if (s0 + u < s_end) {
-                                const float fxv = FU ? fsc[min(r16, M - 1) * kSmallFusedGroups + min(s0 + u, s_end - 1)]
-                                                     : fx[bi][u][t];
-                                const float f = fxv * fw[bi][u][(SG && r >= RH) ? 1 : 0];
-                                acc[r][t].x = __builtin_fmaf(p.x, f, acc[r][t].x);
-                                acc[r][t].y = __builtin_fmaf(p.y, f, acc[r][t].y);
-                                acc[r][t].z = __builtin_fmaf(p.z, f, acc[r][t].z);
-                                acc[r][t].w = __builtin_fmaf(p.w, f, acc[r][t].w);
-                            }
+                            // steps past the wavefront's range multiplied zeros: factor 0
+                            // (branch-free, so every path from the MFMA to its first read
+                            // is the padded one)
+                            const float fxv = FU ? fsc[min(r16, M - 1) * kSmallFusedGroups + min(s0 + u, s_end - 1)]
+                                                 : fx[bi][u][t];
+                            const float f = s0 + u < s_end ? fxv * fw[bi][u][(SG && r >= RH) ? 1 : 0] : 0.0f;
+                            acc[r][t].x = __builtin_fmaf(p.x, f, acc[r][t].x);
+                            acc[r][t].y = __builtin_fmaf(p.y, f, acc[r][t].y);
+                            acc[r][t].z = __builtin_fmaf(p.z, f, acc[r][t].z);
+                            acc[r][t].w = __builtin_fmaf(p.w, f, acc[r][t].w);
                         }
                     }
                 }
@@ -337,6 +338,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
         compute(IC<1>{}, s0 + U);
     }
     if (s0 < s_end) compute(IC<0>{}, s0);
+    mfma_drain();      // the accumulators are stored to LDS next
     __syncthreads();   // every wave is done with its transpose buffer before the reduction reuses it
 
 #pragma unroll
@@ -484,12 +486,6 @@ hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, co
     else QLIN_SMALL(VAR_FP8_BLOCK);
 #undef QLIN_SMALL
     return hipGetLastError();
-}
-
-// Longer rows (the down projections) measured slower rounded inside every
-// workgroup than with the quantizer launch before the kernel.
-bool small_fused_fits(int64_t M, int64_t K) {
-    return M >= 1 && M <= kSmallFusedMaxM && K <= kSmallFusedMaxK;
 }
 
 hipError_t launch_gemm_small_fused(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa,

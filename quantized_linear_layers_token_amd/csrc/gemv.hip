@@ -14,6 +14,7 @@
 // with FMAs.  The per-lane partial sums are reduced across the wave with DPP.
 #include "qlin_device.h"
 #include "qlin_internal.h"
+#include "qlin_rows.h"
 
 namespace qlin {
 
@@ -21,14 +22,6 @@ namespace {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
-
-__device__ __forceinline__ int dot16_i8(const v4u& w, const v4u& x, int acc) {
-    acc = __builtin_amdgcn_sdot4((int)w.x, (int)x.x, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)w.y, (int)x.y, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)w.z, (int)x.z, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)w.w, (int)x.w, acc, false);
-    return acc;
-}
 
 __device__ __forceinline__ float dot4_e4m3(uint32_t w, uint32_t x, float acc) {
     const v2f w01 = e4m3_unpack2<false>(w), w23 = e4m3_unpack2<true>(w);

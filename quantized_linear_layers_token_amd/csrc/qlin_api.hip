@@ -2,10 +2,7 @@
 // synchronization; every check runs before the first launch.
 #include <stdint.h>
 
-#include <hip/hip_runtime.h>
-
 #include "../../include/qlin.h"
-#include "qlin_device.h"
 #include "qlin_internal.h"
 
 namespace {
@@ -136,6 +133,10 @@ qlin_status check_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64
         if (segs[i].n == 0) continue;
         if (!segs[i].q_w || !segs[i].s_w || !segs[i].y) return QLIN_ERR_NULL;
         if (!aligned(segs[i].q_w, 16) || !aligned(segs[i].y, 16) || !aligned(segs[i].s_w, 2)) return QLIN_ERR_ALIGN;
+        // the staging buffers are written while the weights are read
+        const int64_t swi = block ? (segs[i].n / 128) * (K / 128) : segs[i].n;
+        const Range rw = rng(segs[i].q_w, segs[i].n * K), rsw = rng(segs[i].s_w, swi * 2);
+        if (q_x && (overlap(rq, rw) || overlap(rq, rsw) || overlap(rs, rw) || overlap(rs, rsw))) return QLIN_ERR_ALIAS;
         const Range ry = rng(segs[i].y, M * segs[i].n * out_bytes(out));
         if (overlap(ry, rx) || (q_x && (overlap(ry, rq) || overlap(ry, rs)))) return QLIN_ERR_ALIAS;
         for (int j = 0; j < nseg; ++j) {
@@ -151,9 +152,23 @@ qlin_status check_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64
 
 }  // namespace
 
-extern "C" {
+namespace qlin {
 
-qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
+qlin_status linear_validate(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
+                            int32_t nseg, qlin_out out, bool* noop) {
+    return check_linear(scheme, x, M, K, segments, nseg, out, nullptr, nullptr, true, noop);
+}
+
+bool linear_is_one_launch(qlin_scheme scheme, int64_t M, int64_t K, const qlin_segment* segments, int32_t nseg) {
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? VAR_INT8 : scheme == QLIN_SCHEME_FP8_ROWWISE ? VAR_FP8_ROW
+                                                                                                   : VAR_FP8_BLOCK;
+    int64_t rows = 0;   // weight rows of the call (validated separately)
+    if (segments != nullptr && nseg >= 1 && nseg <= QLIN_MAX_SEGMENTS)
+        for (int i = 0; i < nseg; ++i) rows += segments[i].n > 0 ? segments[i].n : 0;
+    return ((M == 1) && (K <= kDecodeMaxK)) || linear_tokens_fits(variant, M, K, rows) || small_fused_fits(M, K);
+}
+
+qlin_status linear_call(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
                         int32_t nseg, qlin_out out, void* q_x, float* s_x, hipStream_t stream) {
     const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
                         : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
@@ -161,7 +176,7 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
     if (segments != nullptr && nseg >= 1 && nseg <= QLIN_MAX_SEGMENTS)
         for (int i = 0; i < nseg; ++i) rows += segments[i].n > 0 ? segments[i].n : 0;
     const bool tokens = qlin::linear_tokens_fits(variant, M, K, rows);
-    const bool fused = ((M == 1) && (K <= qlin::kDecodeMaxK)) || tokens || qlin::small_fused_fits(M, K);
+    const bool fused = linear_is_one_launch(scheme, M, K, segments, nseg);
     bool noop = false;
     const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, q_x, s_x, fused, &noop);
     if (st != QLIN_OK || noop) return st;
@@ -206,6 +221,15 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
         if (s != QLIN_OK) return s;
     }
     return QLIN_OK;
+}
+
+}  // namespace qlin
+
+extern "C" {
+
+qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
+                        int32_t nseg, qlin_out out, void* q_x, float* s_x, hipStream_t stream) {
+    return qlin::linear_call(scheme, x, M, K, segments, nseg, out, q_x, s_x, stream);
 }
 
 

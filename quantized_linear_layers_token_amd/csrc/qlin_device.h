@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qlin_internal.h"
+
 namespace qlin {
 
 typedef int   v4i  __attribute__((ext_vector_type(4)));
@@ -14,11 +16,6 @@ typedef float v4f  __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-enum OutMode : int { OUT_BF16 = 0, OUT_I32 = 1, OUT_F32 = 2,
-                     // gate/up pair: segments 0 and 1 are the gate and up weights (equal
-                     // widths), y[0] receives bf16 silu(gate) * up (swiglu_bf16)
-                     OUT_SWIGLU = 3 };
 
 // A raw buffer descriptor over [base, base + bytes): loads at offsets at or
 // past `bytes` return zero.  Arguments must be wave-uniform; they are moved to
@@ -34,6 +31,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
 
 constexpr int kWave = 64;
 
+// Idle issue slots after the last matrix-core (XDL) instruction of a sequence,
+// before anything else touches its destination registers.  The hardware does
+// not interlock a vector-ALU, LDS or memory access against an XDL result: on
+// CDNA3 the software must leave NumPasses + 3 independent slots, and gfx950
+// needs one more for ops of 4 or more passes (NumPasses + 4: 20 for the
+// 16-pass 32x32x64 E4M3 op, 12 for 32x32x32 int8 and 16x16x128 E4M3, 8 for
+// 16x16x64 int8 and 16x16x32 bf16).  This compiler pads some accumulator
+// reads that follow a loop's last MFMAs with only NumPasses + 3 slots (19
+// after a 32x32x64 E4M3 op in the tiled GEMM's exit path), which let the
+// epilogue read the last registers of the last MFMA before they were written.
+// Three s_nop 7 give 24 slots, enough for every op used here whatever the
+// compiler adds; called once per tile, after the K loop.
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // bf16
 // ---------------------------------------------------------------------------
@@ -41,20 +56,6 @@ constexpr int kWave = 64;
 // Exact widening of a bf16 bit pattern (low 16 bits of b) to f32.
 __device__ __forceinline__ float bf16_lo(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Factors of the activation rounding t = fl32(fl32(x * pre) * inv) for a token
-// (or group) with absmax a (bf16 bits, sign cleared) and range Q: pre = 1,
-// inv = fl32(Q / a); for a < 2^-64, where Q / a can exceed the f32 range,
-// pre = 2^64 and inv = fl32(Q / (a * 2^64)).  Scaling by 2^64 is exact, so
-// wherever Q / a is finite both forms give the same t (the dynamic scale of
-// the W8A8 and FP8 model cards, "Loading": code = x / (a / Q), rounded).
-struct RoundFactor {
-    float pre, inv;
-};
-__device__ __forceinline__ RoundFactor round_factor(uint32_t amax_bits, float q) {
-    const float pre = amax_bits < 0x1F80u ? 0x1p64f : 1.0f;       // 0x1F80: bf16 bits of 2^-64
-    const float a = __uint_as_float(amax_bits << 16) * pre;
-    return RoundFactor{pre, amax_bits == 0 ? 0.0f : q / a};
-}
 // Widening of the high bf16 of a packed pair.
 __device__ __forceinline__ float bf16_hi(uint32_t b) { return __uint_as_float(b & 0xFFFF0000u); }
 

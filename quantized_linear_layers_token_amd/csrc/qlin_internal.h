@@ -1,13 +1,21 @@
 // Launchers shared between the kernel files and the C-ABI layer.  All
 // arguments are validated by the caller (qlin_api.hip) before a launch.
+// Host declarations only (the C-ABI layer also builds as plain host C++).
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
+
+#include "../../include/qlin.h"
 
 namespace qlin {
 
 enum Variant : int { VAR_INT8 = 0, VAR_FP8_ROW = 1, VAR_FP8_BLOCK = 2 };
+
+enum OutMode : int { OUT_BF16 = 0, OUT_I32 = 1, OUT_F32 = 2,
+                     // gate/up pair: segments 0 and 1 are the gate and up weights (equal
+                     // widths), y[0] receives bf16 silu(gate) * up (swiglu_bf16)
+                     OUT_SWIGLU = 3 };
 
 // Weight segments that read the same activation row (e.g. q, k, v): rows of
 // segment i are global rows [start[i], start[i+1]).  Passed by value.
@@ -65,7 +73,16 @@ constexpr int64_t kDecodeMaxK = 16384;   // fused one-row path keeps the quantiz
 // kernel supports up to 8 tokens; the dispatch uses it where it was measured
 // faster than quantizer + matrix-core kernel: 2 tokens.
 constexpr int64_t kLinearTokensMaxM = 2;
-bool linear_tokens_fits(int variant, int64_t M, int64_t K, int64_t rows);
+// Block FP8 rows longer than 8 KiB measured slower here (the per-KiB MFMA,
+// permutation and scale traffic of every token) than on the staged path, and
+// so did calls streaming more than 64 MB of weights (the gate/up pair), where
+// the quantizer launch is amortized and the matrix-core kernel streams faster.
+inline bool linear_tokens_fits(int variant, int64_t M, int64_t K, int64_t rows) {
+    const int64_t kc = (K + 1023) / 1024;
+    if (variant == VAR_FP8_BLOCK && kc > 8) return false;
+    if (rows * K > (int64_t(64) << 20)) return false;
+    return M >= 2 && M <= kLinearTokensMaxM && kc <= 16 && kLinearTokensMaxM * kc <= 64;
+}
 hipError_t launch_linear_tokens(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa, int mode,
                                 uint8_t* qx, float* sx, hipStream_t st);
 
@@ -82,7 +99,11 @@ constexpr int kSmallFusedScaleBytes = (int)kSmallFusedMaxM * kSmallFusedGroups *
 inline size_t small_fused_lds_bytes(int64_t M, int64_t K) {
     return (size_t)kSmallFusedScaleBytes + (size_t)M * (size_t)(((K + 127) & ~int64_t(127)) + 64);
 }
-bool small_fused_fits(int64_t M, int64_t K);
+// Longer rows (the down projections) measured slower rounded inside every
+// workgroup than with the quantizer launch before the kernel.
+inline bool small_fused_fits(int64_t M, int64_t K) {
+    return M >= 1 && M <= kSmallFusedMaxM && K <= kSmallFusedMaxK;
+}
 hipError_t launch_gemm_small_fused(int variant, const uint16_t* x, int64_t M, int64_t K, const SegmentArgs& sa,
                                    int mode, uint8_t* qx_out, float* sx_out, hipStream_t st);
 
@@ -93,6 +114,17 @@ hipError_t launch_weight_only(int variant, const uint16_t* x, int64_t M, int64_t
                               hipStream_t st);
 
 int gemv_rows_per_wave(int64_t N, int64_t K);
+
+// qlin_linear with its arguments: validation, then the launch form the call
+// takes (defined with the C ABI).  linear_is_one_launch: the call runs as one
+// launch and needs no staging buffers.
+bool linear_is_one_launch(qlin_scheme scheme, int64_t M, int64_t K, const qlin_segment* segments, int32_t nseg);
+// Every check of qlin_linear except those of the staging buffers; *noop when
+// the call has nothing to do.
+qlin_status linear_validate(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
+                            int32_t nseg, qlin_out out, bool* noop);
+qlin_status linear_call(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K, const qlin_segment* segments,
+                        int32_t nseg, qlin_out out, void* q_x, float* s_x, hipStream_t stream);
 int small_waves_per_tile(int64_t N, int64_t K);
 
 }  // namespace qlin

@@ -1,49 +1,10 @@
-// Device helpers of the row-streaming kernels (fused one-launch products):
-// rounding a bf16 row to int8 / OCP E4M3 codes the way the standalone
-// quantizers do, and one weight row's products with rounded activations.
+// Device helpers of the row-streaming kernels: one weight row's products with
+// rounded activations (int8 dot products, E4M3 on the matrix cores).
 #pragma once
 
-#include "qlin_device.h"
+#include "qlin_round.h"
 
 namespace qlin {
-
-// absmax over 8 bf16 magnitudes (bit patterns with the sign cleared: for
-// non-negative finite floats the bit order is the value order)
-__device__ __forceinline__ uint32_t chunk_absmax(const v4u& v) {
-    uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
-    uint32_t c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
-    uint32_t m0 = max(a & 0xFFFFu, a >> 16), m1 = max(b & 0xFFFFu, b >> 16);
-    uint32_t m2 = max(c & 0xFFFFu, c >> 16), m3 = max(d & 0xFFFFu, d >> 16);
-    return max(max(m0, m1), max(m2, m3));
-}
-
-template <bool FP8>
-__device__ __forceinline__ void scales_from_absmax(uint32_t amax_bits, float& s, RoundFactor& rf) {
-    const float q = FP8 ? 448.0f : 127.0f;
-    s = __uint_as_float(amax_bits << 16) / q;
-    rf = round_factor(amax_bits, q);
-}
-
-__device__ __forceinline__ uint32_t q4_int8(uint32_t w0, uint32_t w1, RoundFactor rf) {
-    auto q = [rf](float v) {
-        float t = __builtin_rintf((v * rf.pre) * rf.inv);
-        t = fminf(fmaxf(t, -127.0f), 127.0f);
-        return (uint32_t)(uint8_t)(int8_t)(int)t;
-    };
-    return q(bf16_lo(w0)) | (q(bf16_hi(w0)) << 8) | (q(bf16_lo(w1)) << 16) | (q(bf16_hi(w1)) << 24);
-}
-
-__device__ __forceinline__ uint32_t q4_fp8(uint32_t w0, uint32_t w1, RoundFactor rf) {
-    auto c = [rf](float v) { return fminf(fmaxf((v * rf.pre) * rf.inv, -448.0f), 448.0f); };
-    const uint32_t lo = e4m3_pack_lo(c(bf16_lo(w0)), c(bf16_hi(w0)));
-    return e4m3_pack_hi(lo, c(bf16_lo(w1)), c(bf16_hi(w1)));
-}
-
-template <bool FP8>
-__device__ __forceinline__ v2u quant8(const v4u& v, RoundFactor rf) {
-    if constexpr (FP8) return v2u{q4_fp8(v.x, v.y, rf), q4_fp8(v.z, v.w, rf)};
-    else return v2u{q4_int8(v.x, v.y, rf), q4_int8(v.z, v.w, rf)};
-}
 
 __device__ __forceinline__ int dot16_i8(const v4u& w, const v4u& x, int acc) {
     acc = __builtin_amdgcn_sdot4((int)w.x, (int)x.x, acc, false);

@@ -351,6 +351,7 @@ __global__ __launch_bounds__(NW * 64) void wo_small_kernel(const uint16_t* __res
         compute(IC<1>{}, s0 + U);
     }
     if (s0 < s_end) compute(IC<0>{}, s0);
+    mfma_drain();      // the accumulators are stored to LDS next
     __syncthreads();   // every wave is done with its transpose buffer before the reduction reuses it
 
 #pragma unroll

@@ -165,6 +165,13 @@ def test_linear_validation():
     assert lin(0, x, 1, 256, nul, 1, 0, None, None, None) == Q.QLIN_ERR_NULL
     empty = (Seg * 1)(Seg(None, None, None, 0))
     assert lin(0, x, 1, 256, empty, 1, 0, None, None, None) == Q.QLIN_OK             # no rows: no-op
+    # staging buffers overlapping a segment's weights or weight scales
+    one = (Seg * 1)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 64))
+    sx_ok, qx_ok = A + 0xB000000, A + 0xA000000
+    assert lin(0, x, 8, 256, one, 1, 0, A + 0x1000000 + 4096, sx_ok, None) == Q.QLIN_ERR_ALIAS   # q_x in q_w
+    assert lin(0, x, 8, 256, one, 1, 0, A + 0x2000000 - 1024, sx_ok, None) == Q.QLIN_ERR_ALIAS   # q_x over s_w
+    assert lin(0, x, 8, 256, one, 1, 0, qx_ok, A + 0x1000000 + 64, None) == Q.QLIN_ERR_ALIAS     # s_x in q_w
+    assert lin(0, x, 8, 256, one, 1, 0, qx_ok, A + 0x2000000 + 4, None) == Q.QLIN_ERR_ALIAS      # s_x in s_w
 
 
 def test_linear_weight_only_validation():
@@ -213,3 +220,4 @@ def test_library_has_no_unresolved_internal_symbols():
     out = subprocess.run(["nm", "-D", "--undefined-only", Q.LIB_PATH], capture_output=True, text=True).stdout
     bad = [ln for ln in out.splitlines() if "qlin" in ln]
     assert not bad, bad
+

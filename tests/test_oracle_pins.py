@@ -470,6 +470,79 @@ def test_epilogue_order_within_tolerance():
     assert np.all(np.abs(ye_f - yb_f) <= np.abs(y) * 2 ** -7 + 1e-30)
 
 
+def bf16_round(r: Fraction) -> Fraction:
+    """Nearest bf16 value of an exact rational, ties to even (8 significant bits,
+    binary32's exponent range; no overflow)."""
+    if r == 0:
+        return Fraction(0)
+    a = abs(r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, -126) - 7)
+    return (-1 if r < 0 else 1) * round(a / ulp) * ulp
+
+
+def _epilogue_fraction(acc: int, sx: float, sw_bits: int) -> Fraction:
+    """bf16_RNE(fl32(fl32(acc) * fl32(s_x * s_w))), every step an exact rational
+    rounded once."""
+    f = f32_round(Fraction(float(sx)) * bf16_value(sw_bits))
+    return bf16_round(f32_round(f32_round(Fraction(int(acc))) * f))
+
+
+def test_epilogue_f32_order_fraction_bruteforce():
+    # random accumulators over the whole int32 range the products reach, with
+    # rounding ties planted at each of the three rounding steps
+    rng = np.random.default_rng(464)
+    acc = rng.integers(-231225344, 231225345, 160, dtype=np.int64)
+    acc[:8] = [257, -259, 16777217, -16777219, 2 ** 24 + 3, 33554435, 0, -1]    # bf16 ties; f32 ties of acc
+    sx = rng.uniform(1e-3, 0.5, 160).astype(np.float32)
+    sx[:8] = 1.0
+    sx[8:16] = np.float32(1.0 + 2.0 ** -23)                                    # s_x * s_w needs rounding
+    swb = W.scale_bf16(465, 160)
+    swb[:8] = 0x3F80                                                           # s_w = 1
+    swb[8:16] = 0x3F81                                                         # 1 + 2^-7
+    got = O.epilogue_f32_order(acc[:, None], sx, swb)                          # [160, 160]
+    for m in range(0, 160, 7):
+        for n in list(range(16)) + list(range(16, 160, 11)):
+            want = _epilogue_fraction(acc[m], sx[m], int(swb[n]))
+            assert bf16_value(int(got[m, n])) == want, (m, n, acc[m], sx[m], hex(swb[n]))
+    # the ties resolve to even significands
+    assert bf16_value(int(got[0, 0])) == 256 and bf16_value(int(got[1, 0])) == -260
+    assert bf16_value(int(got[2, 0])) == 2 ** 24 and bf16_value(int(got[3, 0])) == -(2 ** 24)
+
+
+def test_epilogue_f32_order_is_not_another_order():
+    # The pin has power: products placed within an f32 ulp of a bf16 rounding
+    # tie, where the order of the roundings decides the bf16 result.  The
+    # oracle must match the Fraction chain on every case and differ from two
+    # plausible other orders on some: fl32(fl32(acc * s_x) * s_w), and one
+    # rounding of the exact product.
+    rng = np.random.default_rng(466)
+    accs, sxs, sws = [], [], []
+    for _ in range(300):
+        acc = int(rng.integers(2 ** 20, 2 ** 27)) * (1 if rng.random() < 0.5 else -1)
+        swb = int(rng.integers(0x3A00, 0x3C00))                       # bf16 scales 4.9e-4 .. 7.8e-3
+        tie = Fraction(2 * int(rng.integers(128, 256)) + 1, 2 ** 9) * Fraction(2) ** int(rng.integers(-4, 6))
+        accs.append(acc)
+        sxs.append(np.float32(float(tie / (abs(acc) * bf16_value(swb)))))
+        sws.append(swb)
+    acc = np.array(accs, np.int64)
+    sx = np.array(sxs, np.float32)
+    sw = np.array(sws, np.uint16)
+    got = np.diag(O.epilogue_f32_order(acc[:, None], sx, sw))
+    differs_b = differs_c = 0
+    for i in range(len(acc)):
+        a, x, w = Fraction(int(acc[i])), Fraction(float(sx[i])), bf16_value(int(sw[i]))
+        chain = _epilogue_fraction(acc[i], sx[i], int(sw[i]))
+        assert bf16_value(int(got[i])) == chain, i
+        differs_b += bf16_round(f32_round(f32_round(a * x) * w)) != chain
+        differs_c += bf16_round(a * x * w) != chain
+    assert differs_b > 0 and differs_c > 0, (differs_b, differs_c)
+
+
 def test_math_constants():
     assert O.Q_E4M3 == float(O.e4m3_decode(np.array([0x7E], np.uint8))[0])
     assert math.isclose(O.Q_INT8, 127.0)
@@ -584,13 +657,36 @@ def test_silu_closed_forms_and_identities():
     assert v == 0.0 and math.copysign(1.0, v) < 0
 
 
-def _bf16_rne_via_f32(v):
-    """bf16 rounding of fp64 values through float32 and the integer
-    round-half-even trick on the f32 bit pattern (a different route from the
-    oracle's)."""
-    u = np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    return ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+def _bf16_rne_via_f64_bits(v):
+    """bf16 rounding of fp64 values in one step, on the fp64 bit pattern:
+    round-half-even of the significand at its 8th bit, then the exponent
+    re-biased from 1023 to 127 (a different route from the oracle's; normal
+    bf16 range and zero only)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    assert np.all((a == 0) | ((a >= 2.0 ** -126) & (a < 2.0 ** 127))), "outside the normal bf16 range"
+    u = v.view(np.uint64)
+    lsb = (u >> np.uint64(45)) & np.uint64(1)
+    r = (u + np.uint64((1 << 44) - 1) + lsb) >> np.uint64(45)      # sign | 11-bit exponent | 7-bit significand
+    sign = (r >> np.uint64(18)) & np.uint64(1)
+    exp = ((r >> np.uint64(7)) & np.uint64(0x7FF)).astype(np.int64)
+    man = r & np.uint64(0x7F)
+    bits = (sign << np.uint64(15)) | (np.where(a == 0, 0, exp - 1023 + 127).astype(np.uint64) << np.uint64(7)) | \
+        np.where(a == 0, np.uint64(0), man)
+    return bits.astype(np.uint16)
+
+
+def test_bf16_single_rounding_helper():
+    # ties and near-ties that a double rounding through f32 would get wrong
+    one = 1.0
+    cases = {one + 2.0 ** -8: 0x3F80,                          # tie -> even (1.0)
+             one + 3 * 2.0 ** -8: 0x3F82,                      # tie -> even (1 + 2^-6)
+             one + 2.0 ** -8 + 2.0 ** -40: 0x3F81,             # just above the tie: up (f32 would drop 2^-40)
+             -(one + 2.0 ** -8 - 2.0 ** -40): 0xBF80,          # just below: down
+             3.0: 0x4040, 0.0: 0x0000}
+    for v, want in cases.items():
+        assert int(_bf16_rne_via_f64_bits(np.array([v]))[0]) == want, v
+    assert int(O.round_to_bf16_bits(np.array([one + 2.0 ** -8 + 2.0 ** -40]))[0]) == 0x3F81
 
 
 @pytest.mark.parametrize("scheme", ["int8", "fp8_rowwise", "fp8_block"])
@@ -614,11 +710,11 @@ def test_swiglu_chain_independent(scheme):
     g = O.bf16_bits_to_f64(g_bits)
     u = O.bf16_bits_to_f64(u_bits)
     assert (g < -2).any() and (np.abs(g) < 2).any() and (g > 2).any(), "inputs span the curved part of silu"
-    s = O.bf16_bits_to_f64(_bf16_rne_via_f32(g * (1.0 + np.tanh(g / 2.0)) / 2.0))
-    want = _bf16_rne_via_f32(s * u)
+    s = O.bf16_bits_to_f64(_bf16_rne_via_f64_bits(g * (1.0 + np.tanh(g / 2.0)) / 2.0))
+    want = _bf16_rne_via_f64_bits(s * u)
     assert np.array_equal(h, want)
     # the intermediate rounding matters: a single rounding of silu(g) * u differs somewhere
-    assert not np.array_equal(h, _bf16_rne_via_f32(g * (1.0 + np.tanh(g / 2.0)) / 2.0 * u))
+    assert not np.array_equal(h, _bf16_rne_via_f64_bits(g * (1.0 + np.tanh(g / 2.0)) / 2.0 * u))
     # gate and up do not commute
     h_swapped = O.swiglu_gate_up(x, up, gate, scheme)[0]
     assert not np.array_equal(h, h_swapped)

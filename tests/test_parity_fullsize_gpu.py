@@ -5,9 +5,10 @@ down), checked on sampled outputs the oracle computes one by one.
 Workloads (shapes from the "Command line" sections of the Llama 3.1 8B W8A8
 and Qwen3 8B FP8 model cards):
   * one W8A8 projection, M = 16, N = K = 4096 (checked in full);
-  * the Llama layer at M in {4, 32} (fused q/k/v and gate/up), W8A8;
+  * the Llama layer at M in {4, 8, 16, 32} (fused q/k/v and gate/up), W8A8,
+    and at M in {4, 32} with FP8 per channel;
   * the Llama layer at M in {512, 1024}, W8A8 and FP8 per channel;
-  * the Qwen3 layer with block FP8 at M in {1, 32, 512}.
+  * the Qwen3 layer with block FP8 at M in {1, 4, 8, 32, 512}.
 Every output of a sampled token row is a function of that row alone (the
 rounding is per token or per 128-input group), so the oracle quantizes only
 the sampled rows and contracts them with the sampled weight rows (whole
@@ -121,9 +122,14 @@ def test_single_projection_m16_full():
     assert np.array_equal(host(yi), acc)
 
 
-@pytest.mark.parametrize("M", [4, 32])
+@pytest.mark.parametrize("M", [4, 8, 16, 32])
 def test_llama_small_m_layer(M):
     assert run_layer(W8A8, W.LLAMA_8B, M, 200 + M) > 0
+
+
+@pytest.mark.parametrize("M", [4, 32])
+def test_llama_fp8_rowwise_small_m_layer(M):
+    assert run_layer(FP8R, W.LLAMA_8B, M, 400 + M) > 0
 
 
 @pytest.mark.parametrize("scheme", [W8A8, FP8R])
@@ -132,6 +138,6 @@ def test_llama_prefill_layer(scheme, M):
     assert run_layer(scheme, W.LLAMA_8B, M, (300 if scheme == W8A8 else 400) + M) > 0
 
 
-@pytest.mark.parametrize("M", [1, 32, 512])
+@pytest.mark.parametrize("M", [1, 4, 8, 32, 512])
 def test_qwen3_block_fp8_layer(M):
     assert run_layer(FP8B, W.QWEN3_8B, M, 500 + M) > 0

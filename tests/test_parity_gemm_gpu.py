@@ -355,3 +355,39 @@ def test_fp8_block_every_tile(M, N, K):
         assert_within_tol(y, y_exact, f"fp8 block tile path {p}")
         yf = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, N, F32, p)
         assert np.all(np.abs(yf - y_exact) <= bound), f"f32 result outside the summation bound (path {p})"
+
+
+# The wide small-M tile (64 weight rows: four MFMA row tiles share each token
+# load) runs for calls with at least 256 such tiles, as the fused gate/up
+# projection of Llama-3.1-8B (N = 2 x 14336, K = 4096) at 2..32 tokens: one
+# token tile up to 16 tokens, two from 17.  Every output is compared.
+WIDE_N, WIDE_K = 28672, 4096
+WIDE_M = [5, 16, 17, 32]
+
+
+@pytest.mark.parametrize("M", WIDE_M)
+def test_int8_small_m_wide_tiles(M):
+    print(f"int8 wide small-M M={M}", flush=True)
+    check_int8(*int8_case(5000 + M, M, WIDE_N, WIDE_K), SMALL)
+
+
+@pytest.mark.parametrize("M", WIDE_M)
+def test_fp8_rowwise_small_m_wide_tiles(M):
+    print(f"fp8 rowwise wide small-M M={M}", flush=True)
+    qx, sx, qw, sw = fp8_row_case(5100 + M, M, WIDE_N, WIDE_K)
+    y_exact = O.rescale_rowwise(O.contract_e4m3(qx, qw), sx, sw)
+    y = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, WIDE_N, BF16, SMALL)
+    assert_within_tol(y, y_exact, f"fp8 rowwise wide small-M M={M}")
+    yf = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, WIDE_N, F32, SMALL)
+    assert np.all(np.abs(yf - y_exact) <= rowwise_bound(qx, qw, sx, sw, SMALL))
+
+
+@pytest.mark.parametrize("M", WIDE_M)
+def test_fp8_block_small_m_wide_tiles(M):
+    print(f"fp8 block wide small-M M={M}", flush=True)
+    qx, sx, qw, sw = fp8_block_case(5200 + M, M, WIDE_N, WIDE_K)
+    y_exact = O.rescale_block(O.contract_e4m3_blocks(qx, qw), sx, sw)
+    y = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, WIDE_N, BF16, SMALL)
+    assert_within_tol(y, y_exact, f"fp8 block wide small-M M={M}")
+    yf = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, WIDE_N, F32, SMALL)
+    assert np.all(np.abs(yf - y_exact) <= block_bound(qx, qw, sx, sw, SMALL))

@@ -98,6 +98,8 @@ CASES = [
     (5, 4096, 384),
     (17, 1152, 256),       # two token tiles
     (3, 512, 8192),        # wide small-M tiles (32 gate + 32 up rows)
+    (8, 4096, 8192),       # staged, wide tiles, one token tile
+    (24, 4096, 8192),      # staged, wide tiles, two token tiles
     (32, 4096, 200),
     (33, 512, 384),        # tiled GEMM
     (100, 1024, 200),      # ragged tiles, I % 8 != 0 stores
@@ -172,7 +174,8 @@ def test_swiglu_validation():
     with pytest.raises(q.QlinError) as e:          # h over the gate weights
         q.qlin_linear_swiglu(W8A8, x, (gq, gs), (uq, us), gq, q_x=qx, s_x=sx)
     assert e.value.status == q.QLIN_ERR_ALIAS
+    sxb = empty(torch, (2, K // 128), torch.float32)
     with pytest.raises(q.QlinError) as e:          # block scheme with I % 128 != 0
-        q.qlin_linear_swiglu(FP8B, x, (gq[:64], gs), (uq[:64], us), h, q_x=qx, s_x=sx)
+        q.qlin_linear_swiglu(FP8B, x, (gq[:64], gs), (uq[:64], us), h, q_x=qx, s_x=sxb)
     assert e.value.status == q.QLIN_ERR_SHAPE
     q.qlin_linear_swiglu(W8A8, x[:0], (gq, gs), (uq, us), h, q_x=qx, s_x=sx)   # M = 0: nothing to do
