@@ -50,7 +50,7 @@ extern "C" {
 /* Same type as HIP's own hipStream_t. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define QLIN_ABI_VERSION 1
+#define QLIN_ABI_VERSION 2
 #define QLIN_MAX_K  131072          /* 127 * 128 * K stays below 2^31 */
 #define QLIN_MAX_MN (1 << 24)
 
@@ -61,7 +61,8 @@ typedef enum qlin_status {
     QLIN_ERR_ALIGN = 3,        /* a pointer misses its required alignment */
     QLIN_ERR_UNSUPPORTED = 4,  /* output mode or forced path not available for this call */
     QLIN_ERR_HIP = 5,          /* the HIP runtime rejected the launch */
-    QLIN_ERR_ALIAS = 6         /* an output range overlaps an input range */
+    QLIN_ERR_ALIAS = 6,        /* an output range overlaps an input range */
+    QLIN_ERR_TOO_LARGE = 7     /* the call needs more staging than qlin_linear_noalloc's fixed scratch */
 } qlin_status;
 
 /* Output element type written to y. */
@@ -278,6 +279,34 @@ qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M,
                                const void* gate_q_w, const uint16_t* gate_s_w,
                                const void* up_q_w, const uint16_t* up_s_w, int64_t I,
                                uint16_t* h, void* q_x, float* s_x, hipStream_t stream);
+
+/* Staging capacity of qlin_linear_noalloc: activation codes (M * K bytes) and
+ * activation scales (M or M * K/128 floats). */
+#define QLIN_NOALLOC_MAX_CODE_BYTES  (16 << 20)
+#define QLIN_NOALLOC_MAX_SCALES      (1 << 20)
+
+/* qlin_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call with the same results, bit for bit, but the quantized-activation
+ * staging buffers come from a fixed scratch array inside the library instead
+ * of q_x / s_x arguments.  The array is a static device variable of
+ * QLIN_NOALLOC_MAX_CODE_BYTES + 4 * QLIN_NOALLOC_MAX_SCALES bytes (20 MiB),
+ * held on every GPU the library runs on until the process ends; its address
+ * is looked up once per device, on the first call there.  Nothing is
+ * allocated or freed, here or later.
+ *   Calls whose staging exceeds the scratch (M * K > QLIN_NOALLOC_MAX_CODE_BYTES,
+ *   or more than QLIN_NOALLOC_MAX_SCALES activation scales) return
+ *   QLIN_ERR_TOO_LARGE before any launch; otherwise validation and errors are
+ *   those of qlin_linear.  The stream's device must be the current device
+ *   (QLIN_ERR_UNSUPPORTED otherwise).
+ *   Every call on one GPU uses that GPU's one scratch array: two calls that
+ *   may run at the same time on one GPU (different streams, or host threads
+ *   enqueuing concurrently) race on it and give wrong results.  Calls in one
+ *   stream are ordered and safe.  The scratch keeps the last call's codes; no
+ *   call relies on its previous contents. */
+qlin_status qlin_linear_noalloc(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                                const qlin_segment* segments, int32_t nseg, qlin_out out,
+                                hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Helpers                                                                */

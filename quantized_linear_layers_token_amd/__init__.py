@@ -14,7 +14,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqlin.so")
 
-QLIN_OK, QLIN_ERR_NULL, QLIN_ERR_SHAPE, QLIN_ERR_ALIGN, QLIN_ERR_UNSUPPORTED, QLIN_ERR_HIP, QLIN_ERR_ALIAS = range(7)
+(QLIN_OK, QLIN_ERR_NULL, QLIN_ERR_SHAPE, QLIN_ERR_ALIGN, QLIN_ERR_UNSUPPORTED, QLIN_ERR_HIP, QLIN_ERR_ALIAS,
+ QLIN_ERR_TOO_LARGE) = range(8)
 OUT_BF16, OUT_I32, OUT_F32 = 0, 1, 2
 SCHEME_W8A8, SCHEME_FP8_ROWWISE, SCHEME_FP8_BLOCK = 0, 1, 2
 MAX_SEGMENTS = 4
@@ -23,7 +24,9 @@ PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_LARGE = 0, 1, 2, 3
 PATH_LARGE_256X128, PATH_LARGE_128X128, PATH_LARGE_128X64, PATH_LARGE_128X256 = 4, 5, 6, 7
 PATH_LARGE_128X128_K2, PATH_LARGE_128X64_K2 = 8, 9
 PATH_LARGE_256X256_W8 = 10   # int8 and FP8 rowwise only
-ABI_VERSION = 1
+ABI_VERSION = 2
+NOALLOC_MAX_CODE_BYTES = 16 << 20    # staging capacity of qlin_linear_noalloc
+NOALLOC_MAX_SCALES = 1 << 20
 MAX_K = 131072
 
 # Exported symbols and their C signatures (restype, argtypes).
@@ -44,6 +47,7 @@ SIGNATURES = {
     "qlin_linear": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P, _P, _P]),
     "qlin_linear_weight_only": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P]),
     "qlin_linear_swiglu": (_S, [_S, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P, _P, _P]),
+    "qlin_linear_noalloc": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P]),
     "qlin_status_string": (ctypes.c_char_p, [_S]),
     "qlin_abi_version": (_S, []),
     "qlin_last_hip_error": (_S, []),
@@ -249,6 +253,17 @@ def qlin_linear(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=No
     arr = segments_array(segments)
     _check(_lib.qlin_linear(scheme, _ptr(x), M, K, arr, len(segments), out, _ptr(q_x), _ptr(s_x),
                             _stream(stream)), "qlin_linear")
+
+
+def qlin_linear_noalloc(scheme, x, segments, out=OUT_BF16, stream=None):
+    """qlin_linear with the library's fixed scratch as staging (no q_x / s_x):
+    for callers that cannot allocate.  Calls that may overlap on one GPU race
+    on the scratch."""
+    M, K = _dims2(x, "x", 2)
+    _args(*_segment_args(scheme, M, K, segments, out), ("x", x, 0, None))
+    arr = segments_array(segments)
+    _check(_lib.qlin_linear_noalloc(scheme, _ptr(x), M, K, arr, len(segments), out, _stream(stream)),
+           "qlin_linear_noalloc")
 
 
 def qlin_linear_weight_only(scheme, x, segments, out=OUT_BF16, stream=None):

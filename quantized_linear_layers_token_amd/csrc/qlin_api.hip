@@ -365,6 +365,8 @@ const char* qlin_status_string(qlin_status status) {
         case QLIN_ERR_UNSUPPORTED: return "QLIN_ERR_UNSUPPORTED: output mode or path not available";
         case QLIN_ERR_HIP: return "QLIN_ERR_HIP: the HIP runtime rejected the launch";
         case QLIN_ERR_ALIAS: return "QLIN_ERR_ALIAS: an output overlaps an input";
+        case QLIN_ERR_TOO_LARGE:
+            return "QLIN_ERR_TOO_LARGE: the call needs more staging than the allocation-free scratch holds";
     }
     return "QLIN_ERR_UNKNOWN";
 }

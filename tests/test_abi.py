@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libqlin.so"
         assert n in Q.SIGNATURES, f"{n} has no binding signature"
@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert Q.status_string(s).startswith("QLIN_")
     assert Q.status_string(99) == "QLIN_ERR_UNKNOWN"
     assert L.qlin_last_hip_error() == 0
@@ -221,3 +221,18 @@ def test_library_has_no_unresolved_internal_symbols():
     bad = [ln for ln in out.splitlines() if "qlin" in ln]
     assert not bad, bad
 
+
+def test_linear_noalloc_refuses_calls_past_its_scratch():
+    # refused before any launch (fake addresses, never dereferenced)
+    Seg = Q.QlinSegment
+    segs = (Seg * 1)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 128))
+    na = L.qlin_linear_noalloc
+    K = 4096
+    M = Q.NOALLOC_MAX_CODE_BYTES // K + 1                        # one token too many
+    assert na(0, A, M, K, segs, 1, 0, None) == Q.QLIN_ERR_TOO_LARGE
+    assert na(2, A, 1 << 20 + 1, 128, segs, 1, 0, None) == Q.QLIN_ERR_TOO_LARGE   # too many scales
+    assert na(0, A, 0, K, segs, 1, 0, None) == Q.QLIN_OK                           # M == 0
+    assert na(0, None, 8, K, segs, 1, 0, None) == Q.QLIN_ERR_NULL                  # qlin_linear's validation
+    assert na(0, A, 8, 250, segs, 1, 0, None) == Q.QLIN_ERR_SHAPE
+    assert na(0, A, 1, 256, None, 1, 0, None) == Q.QLIN_ERR_NULL
+    assert "scratch" in Q.status_string(Q.QLIN_ERR_TOO_LARGE)
