@@ -59,8 +59,17 @@ def parse():
                     help="for hardware-counter runs: a 1 GiB copy (counter calibration), then two eager "
                          "decode steps; prints no JSON")
     ap.add_argument("--prefill-workload", action="store_true",
-                    help="for kernel traces of the prefill path: the M=512 Llama layer set (4 layers, one "
-                         "qlin_linear call per input group), int8 then FP8 rowwise, three eager passes each; "
+                    help="for kernel traces and counters of the prefill path: a 1 GiB copy (counter "
+                         "calibration), then for each variant and M the layer set (4 layers, one qlin_linear "
+                         "call per input group; Qwen3 shapes for fp8_block), three eager passes each; "
+                         "prints no JSON")
+    ap.add_argument("--prefill-variants", default="int8,fp8_row",
+                    help="comma list of int8, fp8_row, fp8_block for --prefill-workload")
+    ap.add_argument("--prefill-m", default="512", help="comma list of token counts for --prefill-workload")
+    ap.add_argument("--smallm-workload", action="store_true",
+                    help="for kernel traces and counters of the small-M path: a 1 GiB copy, then the W8A8 "
+                         "projection M=16 N=K=4096 (32 weight copies) and the W8A8 Llama layer set at M=4, 16, "
+                         "32 (4 layers each), one qlin_linear call per input, three eager passes each; "
                          "prints no JSON")
     return ap.parse_args()
 
@@ -487,17 +496,59 @@ def main():
     torch.cuda.set_device(dev)
     use_graph = not args.no_graph
 
+    def copy_calibration():
+        # a plain copy of known size (1 GiB read + 1 GiB written) for scaling the byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     if args.prefill_workload:
-        for variant in ("int8", "fp8_row"):
-            _, _, fused, _, ops, keep = prefill_layer_set(
-                torch, Q, W, variant, 512, 4, dev, {"int8": 300, "fp8_row": 400}[variant] + 512)
+        copy_calibration()
+        for variant in args.prefill_variants.split(","):
+            for M in (int(m) for m in args.prefill_m.split(",")):
+                _, _, fused, _, ops, keep = prefill_layer_set(
+                    torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
+                torch.cuda.synchronize()
+                for _ in range(3):
+                    fused.run()
+                torch.cuda.synchronize()
+                log(f"prefill workload {variant}: M={M}, 4 layers, {len(fused.calls)} calls per pass x3, "
+                    f"{ops} ops per pass")
+                del keep, fused
+        return
+    if args.smallm_workload:
+        copy_calibration()
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        c1 = Launcher(Q, torch)
+        keep = []
+        for _ in range(32):
+            x = W.torch_x_bf16(torch, gen, 16, 4096, dev)
+            qw = W.torch_w_int8(torch, gen, 4096, 4096, dev)
+            sw = W.torch_scale_bf16(torch, gen, (4096,), dev)
+            y = torch.empty((16, 4096), dtype=torch.int16, device=dev)
+            qx = torch.empty((16, 4096), dtype=torch.uint8, device=dev)
+            sx = torch.empty((16,), dtype=torch.float32, device=dev)
+            keep.append((x, qw, sw, y, qx, sx))
+            c1.linear(Q.SCHEME_W8A8, x, [(qw, sw, y)], qx=qx, sx=sx)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            c1.run()
+        torch.cuda.synchronize()
+        log(f"small-M workload: W8A8 M=16 N=K=4096, {len(c1.calls)} calls per pass x3")
+        del keep, c1
+        for M in (4, 16, 32):
+            Lr, nbytes, ops, keep = layer_set(torch, Q, W, Q.SCHEME_W8A8, W.LLAMA_8B, M, 4, dev, 200 + M)
             torch.cuda.synchronize()
             for _ in range(3):
-                fused.run()
+                Lr.run()
             torch.cuda.synchronize()
-            log(f"prefill workload {variant}: M=512, 4 layers, {len(fused.calls)} calls per pass x3, "
-                f"{ops} ops per pass")
-            del keep, fused
+            log(f"small-M workload: W8A8 Llama layer M={M}, 4 layers, {len(Lr.calls)} calls per pass x3, "
+                f"{nbytes} algorithmic bytes per pass")
+            del Lr, keep
         return
 
     # ---- headline: decode, M = 1, 32 distinct layers -------------------------
@@ -508,11 +559,7 @@ def main():
     if args.pmc_workload:
         # calibration: a plain copy of known size (1 GiB read + 1 GiB written),
         # then the decode step's 128 launches, eagerly so each is its own dispatch
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration()
         for _ in range(2):
             F.run()
         torch.cuda.synchronize()
