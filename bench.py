@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--quick", action="store_true", help="headline only (no secondary sweeps, no CPU baseline)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU-oracle sample")
+    ap.add_argument("--sections", default="shapes,configs,smallm,prefill,cpu",
+                    help="comma list of the secondary legs to run besides the decode headline: shapes "
+                         "(per-shape one-row products), configs (the other workload configurations), "
+                         "smallm (products alone at 4..32 tokens), prefill, cpu (the CPU-oracle baseline)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="for hardware-counter runs: a 1 GiB copy (counter calibration), then two eager "
                          "decode steps; prints no JSON")
@@ -626,7 +630,8 @@ def main():
         "gemv_only_gbs": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
         "gemv_avg_launch_us": round(ms_gemv * 1e3 / len(G.calls), 3)}
     log(f"two-kernel step {ms_two:.4f} ms; gemv-only {secondary['decode_two_kernel']}")
-    if not args.quick:
+    sections = set() if args.quick else set(args.sections.split(","))
+    if "shapes" in sections:
         # per-shape one-row bandwidth (all 32 layers of one projection back to back)
         shape_gbs = {}
         for name, items in per_shape.items():
@@ -639,6 +644,7 @@ def main():
         secondary["decode_gemv_gbs_per_shape"] = shape_gbs
         log(f"per-shape GB/s {shape_gbs}")
 
+    if "configs" in sections:
         # the five workloads' other configurations, each with qlin_linear
         # (quantization included) over distinct weights larger than the MALL
         cfgs = {}
@@ -680,6 +686,7 @@ def main():
             torch.cuda.synchronize()
         secondary["configs_quantized_linear"] = cfgs
 
+    if "smallm" in sections:
         # small batch (M = 4..32) on the fused projections, int8
         small = {}
         gen = torch.Generator(device=dev)
@@ -722,6 +729,7 @@ def main():
         log(f"small-M weight-only {small_wo}")
         del wts
 
+    if "prefill" in sections:
         # prefill TOPS
         for variant, peak in (("int8", MFMA_INT8_PEAK_TOPS), ("fp8_row", MFMA_FP8_PEAK_TOPS),
                               ("fp8_block", MFMA_FP8_PEAK_TOPS)):
@@ -752,7 +760,7 @@ def main():
                 torch.cuda.synchronize()
 
     cpu = None
-    if not args.quick:
+    if "cpu" in sections:
         log("CPU oracle sample")
         cpu, max_rel, exact = cpu_baseline(torch, W, bufs, args.cpu_seconds)
         secondary["max_rel_err_vs_oracle"] = max_rel
