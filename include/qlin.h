@@ -93,7 +93,10 @@ typedef enum qlin_path {
     QLIN_PATH_LARGE_128X64_K2 = 9,
     /* 256 x 256 with 8 wavefronts of 128 x 64, one workgroup per CU; int8 and
      * FP8 rowwise only (QLIN_ERR_UNSUPPORTED for block FP8) */
-    QLIN_PATH_LARGE_256X256_W8 = 10
+    QLIN_PATH_LARGE_256X256_W8 = 10,
+    /* 256 x 256 with 4 wavefronts of 128 x 128 (one per SIMD), one workgroup
+     * per CU; int8 and FP8 rowwise only */
+    QLIN_PATH_LARGE_256X256 = 11
 } qlin_path;
 
 /* ---------------------------------------------------------------------- */

@@ -24,6 +24,7 @@ PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_LARGE = 0, 1, 2, 3
 PATH_LARGE_256X128, PATH_LARGE_128X128, PATH_LARGE_128X64, PATH_LARGE_128X256 = 4, 5, 6, 7
 PATH_LARGE_128X128_K2, PATH_LARGE_128X64_K2 = 8, 9
 PATH_LARGE_256X256_W8 = 10   # int8 and FP8 rowwise only
+PATH_LARGE_256X256 = 11      # int8 and FP8 rowwise only
 ABI_VERSION = 2
 NOALLOC_MAX_CODE_BYTES = 16 << 20    # staging capacity of qlin_linear_noalloc
 NOALLOC_MAX_SCALES = 1 << 20

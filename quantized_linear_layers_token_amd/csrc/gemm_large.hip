@@ -3,20 +3,25 @@
 // accumulation; Qwen3 8B FP8 card, "Loading": block-scaled FP8 product).
 //
 // Tiled GEMM, both operands K-contiguous.  Output tile = BN weight rows x BM
-// tokens, 4 wavefronts (8 for the 256 x 256 tile) in a WN x WM grid; a wave
-// owns a (BN/WN) x (BM/WM) sub-tile of 32 x 32 MFMA tiles:
+// tokens, 4 wavefronts (8 for two K groups or the 8-wave 256 x 256 tile) in a
+// WN x WM grid; a wave owns a (BN/WN) x (BM/WM) sub-tile of 32 x 32 MFMA tiles:
 //   int8: v_mfma_i32_32x32x32_i8      (4 per 128-byte K stage, 32 cycles each)
 //   E4M3: v_mfma_f32_32x32x64_f8f6f4  (2 per 128-byte K stage, 64 cycles each)
-// (32 x 32 tiles need half the LDS operand bytes per MAC of 16 x 16 ones, and
-// large wave tiles keep the operand reads under the ~128 B/clk LDS port).
+// (32 x 32 tiles need half the LDS operand bytes per MAC of 16 x 16 ones.)
+// Unit rates measured on one CU: LDS reads ~240 B/clk, LDS writes (ds_write
+// or direct loads) ~75 B/clk, global loads ~60 B/clk, so a tile's LDS writes
+// and global loads per MFMA cycle are what bigger tiles save.
 //
-// K advances in 128-byte stages.  Pipeline: stage s is loaded from global
-// memory into one of two register sets at iteration s - 2, written to one of
-// two LDS buffers at iteration s - 1, and multiplied at iteration s; one
-// barrier per stage.  Register loads give the compiler exact per-register wait
-// counts, so two stages of loads stay in flight while a stage is multiplied.
-// (Direct global->LDS loads were tried: the compiler then drains every load in
-// flight before any LDS read of the tile.)  LDS rows are 128 bytes with the
+// K advances in 128-byte stages, one barrier per stage.  Register staging
+// (every tile but one): stage s is loaded from global memory into one of two
+// register sets at iteration s - 2, written to one of two LDS buffers at
+// iteration s - 1, and multiplied at iteration s; register loads give the
+// compiler exact per-register wait counts, so two stages of loads stay in
+// flight.  Direct staging (the 4-wavefront 256 x 256 tile): stage s + 1 goes
+// from global memory straight into the other LDS buffer while stage s is
+// multiplied, and the step ends by waiting for it; the two buffers are
+// distinct LDS arrays, so the compiler does not drain those loads before the
+// reads of the current buffer.  LDS rows are 128 bytes with the
 // 16-byte chunk index XOR-swizzled by swz(row) = (row & 7) ^ ((row >> 3) & 1):
 // an MFMA operand read (one logical chunk of 16 consecutive rows per 16-lane
 // phase) hits 16 distinct 16-byte bank groups.
@@ -30,10 +35,13 @@
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8; tile ids are
 // assigned so that tiles sharing a weight panel are consecutive on one XCD.
 //
-// 256 x 256 tile (rowwise schemes): 8 wavefronts of 128 x 64, one workgroup
-// per CU (two wavefronts per SIMD).  It fetches half the bytes per MAC of a
-// 128 x 128 tile; with 128 accumulators per wavefront its operands are read
-// right before their MFMAs instead of one sub-step ahead.
+// 256 x 256 tiles (rowwise schemes), one workgroup per CU; per MAC they fetch
+// and write to LDS half the bytes of a 128 x 128 tile.  With 4 wavefronts of
+// 128 x 128 (one per SIMD, 256 accumulators each) the operands of K sub-step
+// s + 1 are read while the MFMAs of s run.  With 8 wavefronts of 128 x 64 (two
+// per SIMD, 128 accumulators and two staging sets each) there is no room for
+// that read-ahead: operands are read right before their MFMAs and the other
+// wavefront on the SIMD covers the latency.
 //
 // K groups (KG = 2): 512 threads in two groups of four wavefronts; group g
 // multiplies stages g, g + 2, ... of the same tile from its own pair of LDS
@@ -62,9 +70,16 @@ template <> struct LargeAcc<VAR_FP8_BLOCK> { typedef v16f T; };
 
 template <int U> using IC = std::integral_constant<int, U>;
 
+// 16 bytes per lane from a buffer into LDS: lane l's bytes land at dst + 16 l
+// (dst is the same for the whole wave).  A plain device function: inside the
+// kernel's lambdas the builtin would also be seen by the host pass.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int V, int BN, int BM, int WN, int WM, bool SG, int KG>
+template <int V, int BN, int BM, int WN, int WM, bool SG, int KG, bool DM>
 __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa,
     int M, int K, int mode, int tiles_m, int tiles_n) {
@@ -82,9 +97,16 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     // MFMA groups per stage at which loads are issued (see compute)
     constexpr int HOOKS = V == VAR_INT8 ? 4 * TN : (V == VAR_FP8_ROW ? 2 * TN : TN * TM);
     constexpr bool LOWREG = BN == 256 && BM == 256;        // 8 wavefronts of 128 x 64
-    // stage buffers; the bf16 epilogue tile (BM rows of BN bf16 + 16 bytes) reuses them
-    constexpr int LDSB = KG * 2 * STAGE > BM * (BN * 2 + 16) ? KG * 2 * STAGE : BM * (BN * 2 + 16);
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSB];
+    // Two LDS arrays: stage buffer 0 of every K group in ldsA, buffer 1 in
+    // ldsB (distinct arrays, so the compiler knows that the direct loads into
+    // one buffer leave reads of the other alone).  The bf16 epilogue tile (BM
+    // rows of BN bf16 + 16 bytes) reuses them: its first BM/2 rows in ldsA,
+    // the rest in ldsB.
+    constexpr int PITCH = BN * 2 + 16;
+    constexpr int LDSH = KG * STAGE > (BM / 2) * PITCH ? KG * STAGE : (BM / 2) * PITCH;
+    __shared__ __attribute__((aligned(1024))) uint8_t ldsA[LDSH];
+    __shared__ __attribute__((aligned(1024))) uint8_t ldsB[LDSH];
+    auto erow = [&](int r) { return r < BM / 2 ? ldsA + r * PITCH : ldsB + (r - BM / 2) * PITCH; };
     __shared__ float s_w_t[BN], s_x_t[BM];                // rowwise schemes: this tile's scales
 
     const int tid = threadIdx.x;
@@ -145,7 +167,8 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     // LDS buffers; both groups run the same number of steps (barriers are
     // shared), a step past the last stage multiplies a zero stage.
     const int nko = (nk + KG - 1) / KG;
-    uint8_t* const glds = lds + grp * 2 * STAGE;
+    // LDS stage buffer b of this thread's K group
+    auto sbuf = [&](auto b) { return (decltype(b)::value ? ldsB : ldsA) + grp * STAGE; };
     auto gs = [&](int i) { return KG * i + grp; };
     const int kbs = K >> 7;
 
@@ -198,7 +221,7 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     };
     auto write = [&](auto set, auto buf, int s) {
         const v4u(&r)[CH] = decltype(set)::value ? ry : rx;
-        uint8_t* base = glds + decltype(buf)::value * STAGE;
+        uint8_t* base = sbuf(buf);
         if (KG > 1 && s >= nk) {
             // a K group's step past the last stage: zeros
 #pragma unroll
@@ -225,6 +248,54 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
         }
     };
 
+    // Direct staging (DM): the stage goes from global memory straight into
+    // LDS (buffer_load_dwordx4 ... lds).  One instruction of a wave fills 1 KB
+    // of LDS in lane order, i.e. 8 rows of 128 bytes: lane l lands in row
+    // (its carried row), slot l % 8, so it loads logical chunk
+    // (l % 8) ^ swz(row) to keep the swizzled layout.  Chunks at or past K
+    // (the ragged last stage, a K group's step past the end) take an offset
+    // outside the descriptor and land as zeros.
+    constexpr int kOOB = 0x40000000;
+    const int cdma = cthr ^ swz(gtid >> 3);
+    auto dma_one = [&](auto buf, int s, int j) {
+        const int k = s * kBK + (cdma << 4);
+        const bool in = k < K;
+        uint8_t* dst = sbuf(buf) + j * RP * kBK + wave * 1024;
+        if (SG && j >= JW / 2 && j < JW) dma16(du, dst, in ? roff[j - JW / 2] + k : kOOB);
+        else if (j < JW) dma16(dw, dst, in ? roff[j] + k : kOOB);
+        else dma16(dx, dst, in ? roff[j - JW] + k : kOOB);
+    };
+    // block FP8: the stage's factors load straight into the buffer's registers
+    auto dma_fac = [&](auto buf, int s) {
+        if constexpr (V == VAR_FP8_BLOCK) {
+            float(&fx)[TM] = decltype(buf)::value ? fx1 : fx0;
+            float(&fw)[TN] = decltype(buf)::value ? fw1 : fw0;
+            const int kb = min(s, kbs - 1);
+#pragma unroll
+            for (int jj = 0; jj < TM; ++jj)
+                fx[jj] = sx[(int64_t)min(m0 + wm * SM + jj * 32 + (lane & 31), M - 1) * kbs + kb];
+#pragma unroll
+            for (int ii = 0; ii < TN; ++ii) {
+                const int rr = wn * SN + ii * 32;
+                if (SG && rr >= PR) fw[ii] = bf16_lo(sw_u[(int64_t)(min(n0 + rr - PR, N - 1) >> 7) * kbs + kb]);
+                else fw[ii] = bf16_lo(sw[(int64_t)(min(n0 + rr, N - 1) >> 7) * kbs + kb]);
+            }
+        }
+    };
+    // the next stage's loads go out in the first half of this stage's MFMAs,
+    // so they have the second half to land before the closing barrier
+    constexpr int DH = HOOKS / 2 > 0 ? HOOKS / 2 : 1;
+    auto dma_hook = [&](auto buf, int s, int h) {
+        if (h >= DH) return;
+        __builtin_amdgcn_sched_barrier(0);
+        if (h == 0) dma_fac(buf, s);
+#pragma unroll
+        for (int j = h * CH / DH; j < (h + 1) * CH / DH; ++j) dma_one(buf, s, j);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // every direct load of the stage has written LDS (vmcnt 0), before the barrier
+    auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+
     // With 512 threads a wave may hold 256 registers.  Unless AGPRs are known
     // to be in use, the compiler then takes all 256 as VGPRs, selects the
     // VGPR form of the MFMAs and spills; naming one AGPR keeps the
@@ -247,10 +318,17 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
         for (int i = tid; i < BM; i += NTH) s_x_t[i] = sx[min(m0 + i, M - 1)];
     }
 
-    // prologue: stage 0 in LDS buffer 0, stage 1 in flight
-    issue_all(IC<0>{}, gs(0));
-    write(IC<0>{}, IC<0>{}, gs(0));
-    issue_all(IC<1>{}, gs(1));
+    // prologue: stage 0 in LDS buffer 0 (register staging: stage 1 in flight)
+    if constexpr (DM) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) dma_one(IC<0>{}, gs(0), j);
+        dma_fac(IC<0>{}, gs(0));
+        dma_wait();
+    } else {
+        issue_all(IC<0>{}, gs(0));
+        write(IC<0>{}, IC<0>{}, gs(0));
+        issue_all(IC<1>{}, gs(1));
+    }
     __syncthreads();
 
     // A wave issues its stage's MFMAs at raised priority (back to normal for the
@@ -258,9 +336,57 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     // feeding the matrix core while the other wave is in its write phase.
     auto compute = [&](auto buf, const float (&fx)[TM], const float (&fw)[TN], auto&& hk) {
         __builtin_amdgcn_s_setprio(1);
-        const uint8_t* base = glds + decltype(buf)::value * STAGE;
+        const uint8_t* base = sbuf(buf);
         auto rdq = [&](int r, int c) { return *reinterpret_cast<const v4i*>(base + r * kBK + ((c ^ swz(r)) << 4)); };
-        if constexpr (LOWREG) {
+        if constexpr (LOWREG && WN * WM == 4) {
+            // 256 x 256 tiles with one wavefront per SIMD: the operands of K
+            // sub-step s + 1 are read while the MFMAs of s run
+            static_assert(V != VAR_FP8_BLOCK, "rowwise schemes only");
+            constexpr int SUB = V == VAR_INT8 ? 4 : 2;
+            typedef typename std::conditional<V == VAR_INT8, v4i, v8i>::type Op;
+            Op aq[2][TN], bq[2][TM];
+            auto rop = [&](int r, int sub) {
+                if constexpr (V == VAR_INT8) {
+                    return rdq(r, 2 * sub + half);
+                } else {
+                    const int c0 = 4 * sub + 2 * half;
+                    const v4i lo = rdq(r, c0), hi = rdq(r, c0 + 1);
+                    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                }
+            };
+            auto rd = [&](int p, int sub) {
+#pragma unroll
+                for (int j = 0; j < TM; ++j) bq[p][j] = rop(brow0 + j * 32, sub);
+#pragma unroll
+                for (int i = 0; i < TN; ++i) aq[p][i] = rop(arow0 + i * 32, sub);
+            };
+            // (FP8: a sub-step's 16 reads go out after the first MFMAs of the
+            // previous one, so that at most 16 reads wait in the LDS queue)
+            rd(0, 0);
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                if (V == VAR_INT8 && sub + 1 < SUB) rd((sub + 1) & 1, sub + 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+#pragma unroll
+                    for (int j = 0; j < TM; ++j) {
+                        if constexpr (V == VAR_INT8)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aq[sub & 1][i], bq[sub & 1][j], acc[i][j], 0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq[sub & 1][i], bq[sub & 1][j], acc[i][j],
+                                                                                       0, 0, 0, 0, 0, 0);
+                    }
+                    if (V != VAR_INT8 && i == 0 && sub + 1 < SUB) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        rd((sub + 1) & 1, sub + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    hk(sub * TN + i);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if constexpr (LOWREG) {
             // 256 x 256 tiles: 128 accumulators and two staging sets leave no
             // room for a read-ahead, so per K sub-step the token tiles are
             // read once and each weight tile right before its MFMAs (the
@@ -409,16 +535,33 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     // unconditionally: a stage past the end re-reads in-range bytes and
     // writes zeros to a buffer that is not multiplied again (a conditional
     // load makes the compiler assume the shallower pipeline everywhere).
+    //
+    // Direct staging: step kt multiplies buffer kt % 2 while the next stage
+    // loads into the other buffer (free since the previous barrier); the
+    // step ends by waiting for those loads and meeting the barrier.
     int kt = 0;
-    for (; kt + 1 < nko; kt += 2) {
-        compute(IC<0>{}, fx0, fw0, [&](int h) { hook(IC<0>{}, gs(kt + 2), h); });
-        __builtin_amdgcn_s_setprio(0);
-        write(IC<1>{}, IC<1>{}, gs(kt + 1));
-        __syncthreads();
-        compute(IC<1>{}, fx1, fw1, [&](int h) { hook(IC<1>{}, gs(kt + 3), h); });
-        __builtin_amdgcn_s_setprio(0);
-        write(IC<0>{}, IC<0>{}, gs(kt + 2));
-        __syncthreads();
+    if constexpr (DM) {
+        for (; kt + 1 < nko; kt += 2) {
+            compute(IC<0>{}, fx0, fw0, [&](int h) { dma_hook(IC<1>{}, gs(kt + 1), h); });
+            __builtin_amdgcn_s_setprio(0);
+            dma_wait();
+            __syncthreads();
+            compute(IC<1>{}, fx1, fw1, [&](int h) { dma_hook(IC<0>{}, gs(kt + 2), h); });
+            __builtin_amdgcn_s_setprio(0);
+            dma_wait();
+            __syncthreads();
+        }
+    } else {
+        for (; kt + 1 < nko; kt += 2) {
+            compute(IC<0>{}, fx0, fw0, [&](int h) { hook(IC<0>{}, gs(kt + 2), h); });
+            __builtin_amdgcn_s_setprio(0);
+            write(IC<1>{}, IC<1>{}, gs(kt + 1));
+            __syncthreads();
+            compute(IC<1>{}, fx1, fw1, [&](int h) { hook(IC<1>{}, gs(kt + 3), h); });
+            __builtin_amdgcn_s_setprio(0);
+            write(IC<0>{}, IC<0>{}, gs(kt + 2));
+            __syncthreads();
+        }
     }
     // The K-group hand-off and the epilogue read the accumulators next.  The
     // padding sits inside each exit path: the compiler places its accumulator
@@ -434,8 +577,8 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
         // group 1 hands its partial sums to group 0 through LDS (one dword per
         // lane and accumulator element, lane-contiguous), group 0 adds them
         constexpr int NACC = TN * TM * 16;
-        static_assert(WN * WM * NACC * 64 * 4 <= (int)sizeof(lds), "partials fit the stage buffers");
-        uint32_t* part = reinterpret_cast<uint32_t*>(lds) + wave * NACC * 64 + lane;
+        static_assert(WN * WM * NACC * 64 * 4 <= (int)sizeof(ldsA), "partials fit the stage buffers");
+        uint32_t* part = reinterpret_cast<uint32_t*>(ldsA) + wave * NACC * 64 + lane;
         __syncthreads();                                   // both groups are done with their stages
         if (grp == 1) {
 #pragma unroll
@@ -475,8 +618,7 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     // a wave covering 1 KB of contiguous rows per store instead of 32 rows x
     // 16 bytes.
     if (SG || (mode == OUT_BF16 && (N & 7) == 0)) {
-        constexpr int PITCH = BN * 2 + 16;
-        static_assert(BM * PITCH <= (int)sizeof(lds), "bf16 staging tile fits the stage buffers");
+        static_assert((BM / 2) * PITCH <= (int)sizeof(ldsA), "bf16 staging tile fits the stage buffers");
         __syncthreads();                                   // every wave is done with the last stage
         if (grp == 0) {
 #pragma unroll
@@ -497,7 +639,7 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
                     }
                     const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
                     const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    *reinterpret_cast<v2u*>(lds + ml * PITCH + nl * 2) = v2u{lo, hi};
+                    *reinterpret_cast<v2u*>(erow(ml) + nl * 2) = v2u{lo, hi};
                 }
         }
         }
@@ -509,8 +651,8 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
                 const int row = id / CPH, c = id % CPH;
                 const int m = m0 + row, j = n0 + 8 * c;
                 if (m >= M || j >= N) continue;
-                const v4u g = *reinterpret_cast<const v4u*>(lds + row * PITCH + 16 * c);
-                const v4u u = *reinterpret_cast<const v4u*>(lds + row * PITCH + PR * 2 + 16 * c);
+                const v4u g = *reinterpret_cast<const v4u*>(erow(row) + 16 * c);
+                const v4u u = *reinterpret_cast<const v4u*>(erow(row) + PR * 2 + 16 * c);
                 const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
                 uint32_t hw[4];
 #pragma unroll
@@ -535,7 +677,7 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
             const int m = m0 + row, n = n0 + 8 * c;
             if (m < M && n < N)
                 *reinterpret_cast<v4u*>(static_cast<uint16_t*>(y) + (int64_t)m * N + n) =
-                    *reinterpret_cast<const v4u*>(lds + row * PITCH + 16 * c);
+                    *reinterpret_cast<const v4u*>(erow(row) + 16 * c);
         }
         return;
     }
@@ -584,21 +726,21 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     }
 }
 
-template <int V, int BN, int BM, int WN, int WM, int KG = 1>
+template <int V, int BN, int BM, int WN, int WM, int KG = 1, bool DM = false>
 hipError_t launch_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K, int mode,
                        hipStream_t st) {
     const int tm = (int)((M + BM - 1) / BM);
     dim3 block(64 * WN * WM * KG);
     if (mode == OUT_SWIGLU) {
         const int tn = (sa.start[1] + BN / 2 - 1) / (BN / 2);
-        hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, true, KG>), dim3((unsigned)(tm * tn)), block, 0, st, qx,
-                           sx, sa, (int)M, (int)K, mode, tm, tn);
+        hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, true, KG, DM>), dim3((unsigned)(tm * tn)),
+                           block, 0, st, qx, sx, sa, (int)M, (int)K, mode, tm, tn);
         return hipGetLastError();
     }
     int tn = 0;
     for (int i = 0; i < sa.nseg; ++i) tn += (sa.start[i + 1] - sa.start[i] + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, false, KG>), dim3((unsigned)(tm * tn)), block, 0, st, qx, sx,
-                       sa, (int)M, (int)K, mode, tm, tn);
+    hipLaunchKernelGGL((gemm_large_kernel<V, BN, BM, WN, WM, false, KG, DM>), dim3((unsigned)(tm * tn)), block,
+                       0, st, qx, sx, sa, (int)M, (int)K, mode, tm, tn);
     return hipGetLastError();
 }
 
@@ -613,9 +755,15 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
         case kTile128x128K2: return launch_tile<V, 128, 128, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
         case kTile128x64K2: return launch_tile<V, 128, 64, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
         case kTile256x256W8:
-            // block FP8 rescales partial products per stage: no registers left at this tile
+            // block FP8 rescales partial products per stage: no registers left at this tile.
+            // Two wavefronts per SIMD leave no room for a whole stage of operands, which
+            // direct staging needs: register staging.
             if constexpr (V == VAR_FP8_BLOCK) return hipErrorInvalidValue;
             else return launch_tile<V, 256, 256, 2, 4>(qx, sx, sa, M, K, mode, st);
+        case kTile256x256:
+            if constexpr (V == VAR_FP8_BLOCK) return hipErrorInvalidValue;
+            else return launch_tile<V, 256, 256, 2, 2, 1, true>(qx, sx, sa, M, K, mode, st);
+
         default: return hipErrorInvalidValue;
     }
 }
@@ -623,14 +771,20 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
 }  // namespace
 
 // Tile choice, from timings of every tile on the Llama-8B projections at 256,
-// 512, 1024 and 2048 tokens (t = number of 128 x 128 tiles, 256 CUs):
-//   FP8 rowwise with at least 224 tiles of 256 x 256 (7 of 8 CUs busy):
-//     256 x 256 with 8 wavefronts (gate/up at 512 tokens: 76 -> 63 us);
+// 512, 1024 and 2048 tokens (t = number of 128 x 128 tiles, t256 = number of
+// 256 x 256 tiles, 256 CUs):
+//   int8 with t256 >= 224 (7 of 8 CUs busy): 256 x 256 with 4 wavefronts and
+//     direct staging (gate/up at 512 tokens: 80.5 -> 77.1 us, at 1024:
+//     147.9 -> 134.5 us against the 8-wavefront tile);
+//   FP8 rowwise with t256 >= 512: the same tile (8192^2 x 8192: 476 -> 462 us);
+//   FP8 rowwise with 224 <= t256 < 512: 256 x 256 with 8 wavefronts (gate/up
+//     at 512 tokens: 67.8 us against 72.3 for the 4-wavefront tile);
 //   t >= 384: 128 x 128, two workgroups share a CU;
 //   192 <= t < 384: 128 x 128 with two K groups (8 wavefronts, one tile per
 //     CU, two wavefronts per SIMD);
 //   t < 192: 128 x 64 with two K groups.
-// The int8 256 x 256 tile measured no faster than 128 x 128 on any shape.
+// Direct staging lost on every 128-row tile (e.g. int8 down at 512 tokens,
+// 128 x 64 with two K groups: 46 -> 53 us), so those stage through registers.
 // Block FP8 scales every stage's partial products on the vector ALUs; its
 // 128 x 128 tile with two K groups needs more registers than 8 wavefronts
 // leave (it spills), so it keeps 128 x 64, with two K groups below 192 tiles.
@@ -644,7 +798,10 @@ int large_tile_config(int variant, int64_t M, const SegmentArgs& sa) {
     }
     const int64_t t = ((M + 127) / 128) * panels;
     if (variant == VAR_FP8_BLOCK) return t < 192 ? kTile128x64K2 : kTile128x64;
-    if (variant == VAR_FP8_ROW && ((M + 255) / 256) * panels256 >= 224) return kTile256x256W8;
+    const int64_t t256 = ((M + 255) / 256) * panels256;
+    if (variant == VAR_INT8 && t256 >= 224) return kTile256x256;
+    if (variant == VAR_FP8_ROW && t256 >= 512) return kTile256x256;
+    if (variant == VAR_FP8_ROW && t256 >= 224) return kTile256x256W8;
     if (t >= 384) return kTile128x128;
     return t >= 192 ? kTile128x128K2 : kTile128x64K2;
 }

@@ -40,8 +40,9 @@ qlin_status check_product(int variant, const void* q_x, const float* s_x, const 
     if (variant == qlin::VAR_FP8_BLOCK && ((N % 128) != 0 || (K % 128) != 0)) return QLIN_ERR_SHAPE;
     if (out != QLIN_OUT_BF16 && out != QLIN_OUT_F32 && out != QLIN_OUT_I32) return QLIN_ERR_UNSUPPORTED;
     if (out == QLIN_OUT_I32 && variant != qlin::VAR_INT8) return QLIN_ERR_UNSUPPORTED;
-    if (path < QLIN_PATH_AUTO || path > QLIN_PATH_LARGE_256X256_W8) return QLIN_ERR_UNSUPPORTED;
-    if (path == QLIN_PATH_LARGE_256X256_W8 && variant == qlin::VAR_FP8_BLOCK) return QLIN_ERR_UNSUPPORTED;
+    if (path < QLIN_PATH_AUTO || path > QLIN_PATH_LARGE_256X256) return QLIN_ERR_UNSUPPORTED;
+    if ((path == QLIN_PATH_LARGE_256X256_W8 || path == QLIN_PATH_LARGE_256X256) && variant == qlin::VAR_FP8_BLOCK)
+        return QLIN_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) {
         *noop = true;
         return QLIN_OK;

@@ -54,7 +54,8 @@ inline SegmentArgs one_segment(const uint8_t* w, const uint16_t* sw, void* y, in
 // fixed-tile paths of the C ABI.
 enum LargeTile : int {
     kTile256x128 = 0, kTile128x128 = 1, kTile128x64 = 2, kTile128x256 = 3, kTile128x128K2 = 4, kTile128x64K2 = 5,
-    kTile256x256W8 = 6   // rowwise schemes only
+    kTile256x256W8 = 6,  // rowwise schemes only
+    kTile256x256 = 7     // rowwise schemes only
 };
 // The tiled GEMM over every segment of sa (one launch; a weight panel never
 // straddles two segments).  cfg: LargeTile.

@@ -95,7 +95,7 @@ assert call(gemm, A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000,
 assert call(gemm, A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, -1, 4, 256, 0, 0, None) == SHAPE
 assert call(gemm, A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, 4, 4, 131088, 0, 0, None) == SHAPE
 assert call(gemm, A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, 4, 4, 256, 7, 0, None) == UNSUP
-assert call(gemm, A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, 4, 4, 256, 0, 11, None) == UNSUP
+assert call(gemm, A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, 4, 4, 256, 0, 12, None) == UNSUP
 assert call(gemm, A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, 4, 4, 256, 0, -1, None) == UNSUP
 assert call(gemm, A + 1, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, 4, 4, 256, 0, 0, None) == ALIGN
 assert call(gemm, None, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, 4, 4, 256, 0, 0, None) == NULL
@@ -142,7 +142,7 @@ def size():
 for it in range(20000):
     fn = rng.randrange(7)
     M, N, K = size(), size(), rng.choice([16, 128, 256, 4096, 14336, 250, 0, -16, 131072, 131200])
-    out, path = rng.choice([0, 1, 2, 3, -1]), rng.choice(list(range(0, 11)) + [-1, 11, 99])
+    out, path = rng.choice([0, 1, 2, 3, -1]), rng.choice(list(range(0, 12)) + [-1, 12, 99])
     scheme = rng.choice([0, 1, 2, 3, -1])
     if fn == 0:
         call("qlin_quant_act_int8", ptr(), M, K, ptr(), ptr(), None)

@@ -94,9 +94,10 @@ def test_product_validation(fn):
     assert gemm(fn, *args[:4], b["y"] + 2, 4, 256, 256) == Q.QLIN_ERR_ALIGN
     assert gemm(fn, *args[:3], b["sw"] + 1, b["y"], 4, 256, 256) == Q.QLIN_ERR_ALIGN
     assert gemm(fn, *args, 4, 256, 256, out=7) == Q.QLIN_ERR_UNSUPPORTED
-    assert gemm(fn, *args, 4, 256, 256, path=11) == Q.QLIN_ERR_UNSUPPORTED
+    assert gemm(fn, *args, 4, 256, 256, path=12) == Q.QLIN_ERR_UNSUPPORTED
     if fn == "qlin_gemm_fp8_block":
         assert gemm(fn, *args, 4, 256, 256, path=Q.PATH_LARGE_256X256_W8) == Q.QLIN_ERR_UNSUPPORTED
+        assert gemm(fn, *args, 4, 256, 256, path=Q.PATH_LARGE_256X256) == Q.QLIN_ERR_UNSUPPORTED
     assert gemm(fn, *args, 4, 256, 256, path=-1) == Q.QLIN_ERR_UNSUPPORTED
     assert gemm(fn, *args, 2, 256, 256, path=Q.PATH_GEMV) == Q.QLIN_ERR_UNSUPPORTED
     assert gemm(fn, *args, 33, 256, 256, path=Q.PATH_SMALL) == Q.QLIN_ERR_UNSUPPORTED
