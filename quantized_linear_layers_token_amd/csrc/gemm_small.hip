@@ -464,9 +464,13 @@ hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, co
         return hipGetLastError();
     }
     // 64-row tiles share each token load four ways, but only pay off with at
-    // least a workgroup per CU for every 64 rows (the wide gate/up launch)
+    // least a workgroup per CU for every 64 rows (the wide gate/up launch).
+    // 32-row tiles, with at least 192 of them and K <= 4096: q/k/v (6144 rows)
+    // at 8 / 16 / 32 tokens took 8.9 / 10.0 / 12.2 -> 7.7 / 8.8 / 9.5 us; with
+    // 128 tiles (4096 rows) they lost (6.4 -> 7.0 us at 8 tokens).
     const bool wide = small_tiles(sa, 64) >= 256;
-    const int64_t tiles = small_tiles(sa, wide ? 64 : 16);
+    const bool mid = !wide && K <= 4096 && small_tiles(sa, 32) >= 192;
+    const int64_t tiles = small_tiles(sa, wide ? 64 : (mid ? 32 : 16));
     dim3 grid((unsigned)tiles);
     const int nw = small_waves_per_tile(tiles, K);
     const int m = (int)M, k = (int)K;
@@ -476,6 +480,9 @@ hipError_t launch_gemm_small(int variant, const uint8_t* qx, const float* sx, co
         if (wide) {                                                                   \
             if (two) launch_mt<VV, 2, 4>(nw, grid, st, qx, sx, sa, m, k, mode);       \
             else launch_mt<VV, 1, 4>(nw, grid, st, qx, sx, sa, m, k, mode);           \
+        } else if (mid) {                                                             \
+            if (two) launch_mt<VV, 2, 2>(nw, grid, st, qx, sx, sa, m, k, mode);       \
+            else launch_mt<VV, 1, 2>(nw, grid, st, qx, sx, sa, m, k, mode);           \
         } else {                                                                      \
             if (two) launch_mt<VV, 2, 1>(nw, grid, st, qx, sx, sa, m, k, mode);       \
             else launch_mt<VV, 1, 1>(nw, grid, st, qx, sx, sa, m, k, mode);           \

@@ -391,3 +391,38 @@ def test_fp8_block_small_m_wide_tiles(M):
     assert_within_tol(y, y_exact, f"fp8 block wide small-M M={M}")
     yf = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, WIDE_N, F32, SMALL)
     assert np.all(np.abs(yf - y_exact) <= block_bound(qx, qw, sx, sw, SMALL))
+
+
+# The 32-row small-M tile (two MFMA row tiles share each token load) runs for
+# calls with at least 192 such tiles and K <= 4096 that have too few 64-row
+# tiles, as the fused q/k/v projection of Llama-3.1-8B (N = 6144, K = 4096).
+# A ragged last tile (N = 6160) and ragged K for the rowwise schemes.
+MID_M = [5, 16, 17, 32]
+
+
+@pytest.mark.parametrize("M", MID_M)
+def test_int8_small_m_mid_tiles(M):
+    print(f"int8 32-row small-M M={M}", flush=True)
+    check_int8(*int8_case(5300 + M, M, 6160, 4000), SMALL)
+
+
+@pytest.mark.parametrize("M", MID_M)
+def test_fp8_rowwise_small_m_mid_tiles(M):
+    print(f"fp8 rowwise 32-row small-M M={M}", flush=True)
+    qx, sx, qw, sw = fp8_row_case(5400 + M, M, 6160, 4000)
+    y_exact = O.rescale_rowwise(O.contract_e4m3(qx, qw), sx, sw)
+    y = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, 6160, BF16, SMALL)
+    assert_within_tol(y, y_exact, f"fp8 rowwise 32-row small-M M={M}")
+    yf = run_product("qlin_gemm_fp8_rowwise", qx, sx, qw, sw, M, 6160, F32, SMALL)
+    assert np.all(np.abs(yf - y_exact) <= rowwise_bound(qx, qw, sx, sw, SMALL))
+
+
+@pytest.mark.parametrize("M", MID_M)
+def test_fp8_block_small_m_mid_tiles(M):
+    print(f"fp8 block 32-row small-M M={M}", flush=True)
+    qx, sx, qw, sw = fp8_block_case(5500 + M, M, 6144, 4096)
+    y_exact = O.rescale_block(O.contract_e4m3_blocks(qx, qw), sx, sw)
+    y = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, 6144, BF16, SMALL)
+    assert_within_tol(y, y_exact, f"fp8 block 32-row small-M M={M}")
+    yf = run_product("qlin_gemm_fp8_block", qx, sx, qw, sw, M, 6144, F32, SMALL)
+    assert np.all(np.abs(yf - y_exact) <= block_bound(qx, qw, sx, sw, SMALL))
