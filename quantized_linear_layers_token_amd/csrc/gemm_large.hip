@@ -747,13 +747,16 @@ hipError_t launch_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa
 template <int V>
 hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K,
                           int mode, hipStream_t st) {
+    constexpr bool BD = V == VAR_FP8_BLOCK;
     switch (cfg) {
-        case kTile256x128: return launch_tile<V, 256, 128, 2, 2>(qx, sx, sa, M, K, mode, st);
-        case kTile128x128: return launch_tile<V, 128, 128, 2, 2>(qx, sx, sa, M, K, mode, st);
-        case kTile128x64: return launch_tile<V, 128, 64, 2, 2>(qx, sx, sa, M, K, mode, st);
-        case kTile128x256: return launch_tile<V, 128, 256, 2, 2>(qx, sx, sa, M, K, mode, st);
-        case kTile128x128K2: return launch_tile<V, 128, 128, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
-        case kTile128x64K2: return launch_tile<V, 128, 64, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
+        // block FP8 stages straight into LDS on every tile: its per-stage
+        // rescale needs the registers that register staging would take
+        case kTile256x128: return launch_tile<V, 256, 128, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
+        case kTile128x128: return launch_tile<V, 128, 128, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
+        case kTile128x64: return launch_tile<V, 128, 64, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
+        case kTile128x256: return launch_tile<V, 128, 256, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
+        case kTile128x128K2: return launch_tile<V, 128, 128, 2, 2, 2, BD>(qx, sx, sa, M, K, mode, st);
+        case kTile128x64K2: return launch_tile<V, 128, 64, 2, 2, 2, BD>(qx, sx, sa, M, K, mode, st);
         case kTile256x256W8:
             // block FP8 rescales partial products per stage: no registers left at this tile.
             // Two wavefronts per SIMD leave no room for a whole stage of operands, which
@@ -783,11 +786,14 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
 //   192 <= t < 384: 128 x 128 with two K groups (8 wavefronts, one tile per
 //     CU, two wavefronts per SIMD);
 //   t < 192: 128 x 64 with two K groups.
-// Direct staging lost on every 128-row tile (e.g. int8 down at 512 tokens,
-// 128 x 64 with two K groups: 46 -> 53 us), so those stage through registers.
-// Block FP8 scales every stage's partial products on the vector ALUs; its
-// 128 x 128 tile with two K groups needs more registers than 8 wavefronts
-// leave (it spills), so it keeps 128 x 64, with two K groups below 192 tiles.
+// Direct staging lost on every 128-row tile of the rowwise schemes (e.g. int8
+// down at 512 tokens, 128 x 64 with two K groups: 46 -> 53 us), so those stage
+// through registers.  Block FP8 scales every stage's partial products on the
+// vector ALUs: with register staging its 128 x 128 tiles spill; with direct
+// staging it runs 128 x 128 for t >= 1024 (Qwen3 gate/up at 1024 tokens:
+// 196.8 us for 128 x 64 with register staging -> 158.7 us), else 128 x 64,
+// with two K groups below 192 tiles (direct staging took Qwen3 q/k/v at 1024
+// tokens from 51.5 to 43.9 us).
 // The 256 x 128 tiles (4 or 8 wavefronts) lost on the Llama shapes at 512 and
 // 1024 tokens.
 int large_tile_config(int variant, int64_t M, const SegmentArgs& sa) {
@@ -797,7 +803,7 @@ int large_tile_config(int variant, int64_t M, const SegmentArgs& sa) {
         panels256 += (sa.start[i + 1] - sa.start[i] + 255) / 256;
     }
     const int64_t t = ((M + 127) / 128) * panels;
-    if (variant == VAR_FP8_BLOCK) return t < 192 ? kTile128x64K2 : kTile128x64;
+    if (variant == VAR_FP8_BLOCK) return t >= 1024 ? kTile128x128 : (t < 192 ? kTile128x64K2 : kTile128x64);
     const int64_t t256 = ((M + 255) / 256) * panels256;
     if (variant == VAR_INT8 && t256 >= 224) return kTile256x256;
     if (variant == VAR_FP8_ROW && t256 >= 512) return kTile256x256;
