@@ -311,21 +311,26 @@ __global__ __launch_bounds__(64 * WN * WM * KG) void gemm_large_kernel(
     const int brow0 = BN + wm * SM + (lane & 31);
     const int half = lane >> 5;
 
-    if constexpr (V != VAR_FP8_BLOCK) {
-        // the epilogue's scales, staged once
-        for (int i = tid; i < BN; i += NTH)
-            s_w_t[i] = (SG && i >= PR) ? bf16_lo(sw_u[min(n0 + i - PR, N - 1)]) : bf16_lo(sw[min(n0 + i, N - 1)]);
-        for (int i = tid; i < BM; i += NTH) s_x_t[i] = sx[min(m0 + i, M - 1)];
-    }
+    // the epilogue's scales, staged once; their loads go out after the first
+    // stage's, so that both wait for memory together
+    auto stage_scales = [&]() {
+        if constexpr (V != VAR_FP8_BLOCK) {
+            for (int i = tid; i < BN; i += NTH)
+                s_w_t[i] = (SG && i >= PR) ? bf16_lo(sw_u[min(n0 + i - PR, N - 1)]) : bf16_lo(sw[min(n0 + i, N - 1)]);
+            for (int i = tid; i < BM; i += NTH) s_x_t[i] = sx[min(m0 + i, M - 1)];
+        }
+    };
 
     // prologue: stage 0 in LDS buffer 0 (register staging: stage 1 in flight)
     if constexpr (DM) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) dma_one(IC<0>{}, gs(0), j);
         dma_fac(IC<0>{}, gs(0));
+        stage_scales();
         dma_wait();
     } else {
         issue_all(IC<0>{}, gs(0));
+        stage_scales();
         write(IC<0>{}, IC<0>{}, gs(0));
         issue_all(IC<1>{}, gs(1));
     }
