@@ -754,14 +754,16 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
                           int mode, hipStream_t st) {
     constexpr bool BD = V == VAR_FP8_BLOCK;
     switch (cfg) {
-        // block FP8 stages straight into LDS on every tile: its per-stage
-        // rescale needs the registers that register staging would take
+        // block FP8 stages straight into LDS on the one-group tiles: its
+        // per-stage rescale needs the registers that register staging would
+        // take (the two-group tiles keep register staging: direct staging made
+        // Qwen3 o and down at 512 tokens slower, 22.7 -> 27.7 and 63.3 -> 77.6 us)
         case kTile256x128: return launch_tile<V, 256, 128, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
         case kTile128x128: return launch_tile<V, 128, 128, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
         case kTile128x64: return launch_tile<V, 128, 64, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
         case kTile128x256: return launch_tile<V, 128, 256, 2, 2, 1, BD>(qx, sx, sa, M, K, mode, st);
-        case kTile128x128K2: return launch_tile<V, 128, 128, 2, 2, 2, BD>(qx, sx, sa, M, K, mode, st);
-        case kTile128x64K2: return launch_tile<V, 128, 64, 2, 2, 2, BD>(qx, sx, sa, M, K, mode, st);
+        case kTile128x128K2: return launch_tile<V, 128, 128, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
+        case kTile128x64K2: return launch_tile<V, 128, 64, 2, 2, 2>(qx, sx, sa, M, K, mode, st);
         case kTile256x256W8:
             // block FP8 rescales partial products per stage: no registers left at this tile.
             // Two wavefronts per SIMD leave no room for a whole stage of operands, which
@@ -796,9 +798,9 @@ hipError_t launch_variant(int cfg, const uint8_t* qx, const float* sx, const Seg
 // through registers.  Block FP8 scales every stage's partial products on the
 // vector ALUs: with register staging its 128 x 128 tiles spill; with direct
 // staging it runs 128 x 128 for t >= 1024 (Qwen3 gate/up at 1024 tokens:
-// 196.8 us for 128 x 64 with register staging -> 158.7 us), else 128 x 64,
-// with two K groups below 192 tiles (direct staging took Qwen3 q/k/v at 1024
-// tokens from 51.5 to 43.9 us).
+// 196.8 us for 128 x 64 with register staging -> 158.7 us), else 128 x 64
+// (direct staging took Qwen3 q/k/v at 1024 tokens from 51.5 to 43.9 us), with
+// two K groups and register staging below 192 tiles.
 // The 256 x 128 tiles (4 or 8 wavefronts) lost on the Llama shapes at 512 and
 // 1024 tokens.
 int large_tile_config(int variant, int64_t M, const SegmentArgs& sa) {
