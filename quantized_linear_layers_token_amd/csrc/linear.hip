@@ -30,6 +30,34 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Entry i (< kMaxSegments) of a kernel-argument array, picked by selects over
+// entries loaded at static offsets: the compiler then loads the whole array
+// with the other kernel arguments instead of computing an address and loading
+// once more, a dependent scalar load at the start of every workgroup (the empty
+// asm keeps it from turning the selects back into that load).  Pointers come
+// back as global-memory pointers, so their loads stay global loads.
+__device__ __forceinline__ int pick_int(const int* a, int i) {
+    int v = 0;
+#pragma unroll
+    for (int t = 0; t < kMaxSegments; ++t) {
+        int e = a[t];
+        asm volatile("" : "+s"(e));
+        v = (i == t) ? e : v;
+    }
+    return v;
+}
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* pick_global(const T* const* a, int i) {
+    uint64_t v = 0;
+#pragma unroll
+    for (int t = 0; t < kMaxSegments; ++t) {
+        uint64_t e = reinterpret_cast<uint64_t>(a[t]);
+        asm volatile("" : "+s"(e));
+        v = (i == t) ? e : v;
+    }
+    return reinterpret_cast<const __attribute__((address_space(1))) T*>(v);
+}
+
 // V: scheme; KC: 1 KiB slices per row in registers (K <= 1024 KC); R: rows
 // (SG: gate/up row pairs) per wave per iteration; SG: SwiGLU mode.  CPT = bf16
 // chunks of 8 per thread for the rounding.
@@ -61,11 +89,14 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
 #pragma unroll
     for (int j = 0; j < CPT; ++j) xb[j] = xv[min(tid + j * kThreads, nchunks - 1)];
 
-    const int ntot = SG ? sa.start[1] : sa.start[sa.nseg];   // work items: rows, or gate/up pairs
-    const int W = gridDim.x * (kThreads / kWave);
-    const int w = blockIdx.x * (kThreads / kWave) + wave;
-    const int rb = (int)((int64_t)ntot * w / W);
-    const int re = (int)((int64_t)ntot * (w + 1) / W);
+    const int ntot = SG ? sa.start[1] : pick_int(sa.start + 1, sa.nseg - 1);   // work items: rows, or gate/up pairs
+    // wave w takes items [rb, re): q or q + 1 of them (the first ntot % W waves
+    // one more), in 32-bit arithmetic
+    const unsigned W = gridDim.x * (kThreads / kWave);
+    const unsigned w = blockIdx.x * (kThreads / kWave) + wave;
+    const unsigned q = (unsigned)ntot / W, qr = (unsigned)ntot - q * W;
+    const int rb = (int)(w * q + min(w, qr));
+    const int re = rb + (int)q + (w < qr ? 1 : 0);
 
     auto seg_of = [&](int r) {
         int i = 0;
@@ -85,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         } else {
             const int n = max(min(n0 + r, re - 1), 0);
             i = seg_of(n);
-            local = n - sa.start[i];
+            local = n - pick_int(sa.start, i);
         }
     };
     // block FP8: with its weights, the row's weight-block scales, lane l holding
@@ -97,7 +128,8 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         for (int r = 0; r < RL; ++r) {
             int i, local;
             row_of(r, n0, i, local);
-            const v4u* wrow = reinterpret_cast<const v4u*>(sa.w[i] + (int64_t)local * K);
+            const __attribute__((address_space(1))) v4u* wrow =
+                reinterpret_cast<const __attribute__((address_space(1))) v4u*>(pick_global(sa.w, i) + (int64_t)local * K);
 #pragma unroll
             for (int j = 0; j < SL; ++j) dst[r][j] = __builtin_nontemporal_load(wrow + min(slot(j), k16 - 1));
             if constexpr (V == VAR_FP8_BLOCK) {
