@@ -106,10 +106,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
             }
         }
     }
-    const uint8_t* __restrict__ qw = sa.w[seg];
-    const uint16_t* __restrict__ sw = sa.sw[seg];
-    void* __restrict__ y = sa.y[seg];
-    const int N = sa.start[seg + 1] - sa.start[seg];
+    const uint8_t* __restrict__ qw = pick_ptr(sa.w, seg);
+    const uint16_t* __restrict__ sw = pick_ptr(sa.sw, seg);
+    void* __restrict__ y = pick_ptr(sa.y, seg);
+    const int N = pick_int(sa.start + 1, seg) - pick_int(sa.start, seg);
     const int n0 = __builtin_amdgcn_readfirstlane(tile * TR);
 
     const int nsteps = (K + 127) >> 7;

@@ -30,34 +30,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Entry i (< kMaxSegments) of a kernel-argument array, picked by selects over
-// entries loaded at static offsets: the compiler then loads the whole array
-// with the other kernel arguments instead of computing an address and loading
-// once more, a dependent scalar load at the start of every workgroup (the empty
-// asm keeps it from turning the selects back into that load).  Pointers come
-// back as global-memory pointers, so their loads stay global loads.
-__device__ __forceinline__ int pick_int(const int* a, int i) {
-    int v = 0;
-#pragma unroll
-    for (int t = 0; t < kMaxSegments; ++t) {
-        int e = a[t];
-        asm volatile("" : "+s"(e));
-        v = (i == t) ? e : v;
-    }
-    return v;
-}
-template <class T>
-__device__ __forceinline__ const __attribute__((address_space(1))) T* pick_global(const T* const* a, int i) {
-    uint64_t v = 0;
-#pragma unroll
-    for (int t = 0; t < kMaxSegments; ++t) {
-        uint64_t e = reinterpret_cast<uint64_t>(a[t]);
-        asm volatile("" : "+s"(e));
-        v = (i == t) ? e : v;
-    }
-    return reinterpret_cast<const __attribute__((address_space(1))) T*>(v);
-}
-
 // V: scheme; KC: 1 KiB slices per row in registers (K <= 1024 KC); R: rows
 // (SG: gate/up row pairs) per wave per iteration; SG: SwiGLU mode.  CPT = bf16
 // chunks of 8 per thread for the rounding.
@@ -133,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
 #pragma unroll
             for (int j = 0; j < SL; ++j) dst[r][j] = __builtin_nontemporal_load(wrow + min(slot(j), k16 - 1));
             if constexpr (V == VAR_FP8_BLOCK) {
-                const uint16_t* swr = sa.sw[i] + (int64_t)(local >> 7) * kbs;
+                const __attribute__((address_space(1))) uint16_t* swr = pick_global(sa.sw, i) + (int64_t)(local >> 7) * kbs;
 #pragma unroll
                 for (int q = 0; q < NF; ++q) fsw[r][q] = swr[min(64 * q + lane, kbs - 1)];
             }

@@ -31,6 +31,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
 
 constexpr int kWave = 64;
 
+// Entry i (< kMaxSegments) of a kernel-argument array, picked by selects over
+// entries loaded at static offsets: the compiler then loads the whole array
+// with the other kernel arguments instead of computing an address and loading
+// once more, a dependent scalar load at the start of every workgroup (the empty
+// asm keeps it from turning the selects back into that load).  pick_global
+// returns a global-memory pointer, so that loads through it stay global loads.
+__device__ __forceinline__ int pick_int(const int* a, int i) {
+    int v = 0;
+#pragma unroll
+    for (int t = 0; t < kMaxSegments; ++t) {
+        int e = a[t];
+        asm volatile("" : "+s"(e));
+        v = (i == t) ? e : v;
+    }
+    return v;
+}
+template <class T>
+__device__ __forceinline__ T* pick_ptr(T* const* a, int i) {
+    uint64_t v = 0;
+#pragma unroll
+    for (int t = 0; t < kMaxSegments; ++t) {
+        uint64_t e = reinterpret_cast<uint64_t>(a[t]);
+        asm volatile("" : "+s"(e));
+        v = (i == t) ? e : v;
+    }
+    return reinterpret_cast<T*>(v);
+}
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* pick_global(const T* const* a, int i) {
+    uint64_t v = 0;
+#pragma unroll
+    for (int t = 0; t < kMaxSegments; ++t) {
+        uint64_t e = reinterpret_cast<uint64_t>(a[t]);
+        asm volatile("" : "+s"(e));
+        v = (i == t) ? e : v;
+    }
+    return reinterpret_cast<const __attribute__((address_space(1))) T*>(v);
+}
+
 // Idle issue slots after the last matrix-core (XDL) instruction of a sequence,
 // before anything else touches its destination registers.  The hardware does
 // not interlock a vector-ALU, LDS or memory access against an XDL result: on
