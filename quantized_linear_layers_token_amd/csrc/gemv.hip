@@ -23,24 +23,6 @@ namespace {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 
-__device__ __forceinline__ float dot4_e4m3(uint32_t w, uint32_t x, float acc) {
-    const v2f w01 = e4m3_unpack2<false>(w), w23 = e4m3_unpack2<true>(w);
-    const v2f x01 = e4m3_unpack2<false>(x), x23 = e4m3_unpack2<true>(x);
-    acc = __builtin_fmaf(w01.x, x01.x, acc);
-    acc = __builtin_fmaf(w01.y, x01.y, acc);
-    acc = __builtin_fmaf(w23.x, x23.x, acc);
-    acc = __builtin_fmaf(w23.y, x23.y, acc);
-    return acc;
-}
-
-__device__ __forceinline__ float dot16_e4m3(const v4u& w, const v4u& x) {
-    float a = dot4_e4m3(w.x, x.x, 0.0f);
-    float b = dot4_e4m3(w.y, x.y, 0.0f);
-    a = dot4_e4m3(w.z, x.z, a);
-    b = dot4_e4m3(w.w, x.w, b);
-    return a + b;
-}
-
 // V: VAR_INT8 / VAR_FP8_ROW / VAR_FP8_BLOCK.  KC: 1 KiB chunks per row held in
 // registers (K <= 1024 KC).  R: rows per wave.
 template <int V, int KC, int R>

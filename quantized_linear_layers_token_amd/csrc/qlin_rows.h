@@ -1,5 +1,6 @@
 // Device helpers of the row-streaming kernels: one weight row's products with
-// rounded activations (int8 dot products, E4M3 on the matrix cores).
+// rounded activations (int8 dot products, E4M3 on the vector ALUs or the
+// matrix cores).
 #pragma once
 
 #include "qlin_round.h"
@@ -12,6 +13,27 @@ __device__ __forceinline__ int dot16_i8(const v4u& w, const v4u& x, int acc) {
     acc = __builtin_amdgcn_sdot4((int)w.z, (int)x.z, acc, false);
     acc = __builtin_amdgcn_sdot4((int)w.w, (int)x.w, acc, false);
     return acc;
+}
+
+// E4M3 products on the vector ALUs: byte pairs decoded to f32
+// (v_cvt_pk_f32_fp8; every product of two E4M3 values is exact in f32) and
+// summed with FMAs, two chains per 16 bytes.
+__device__ __forceinline__ float dot4_e4m3(uint32_t w, uint32_t x, float acc) {
+    const v2f w01 = e4m3_unpack2<false>(w), w23 = e4m3_unpack2<true>(w);
+    const v2f x01 = e4m3_unpack2<false>(x), x23 = e4m3_unpack2<true>(x);
+    acc = __builtin_fmaf(w01.x, x01.x, acc);
+    acc = __builtin_fmaf(w01.y, x01.y, acc);
+    acc = __builtin_fmaf(w23.x, x23.x, acc);
+    acc = __builtin_fmaf(w23.y, x23.y, acc);
+    return acc;
+}
+
+__device__ __forceinline__ float dot16_e4m3(const v4u& w, const v4u& x) {
+    float a = dot4_e4m3(w.x, x.x, 0.0f);
+    float b = dot4_e4m3(w.y, x.y, 0.0f);
+    a = dot4_e4m3(w.z, x.z, a);
+    b = dot4_e4m3(w.w, x.w, b);
+    return a + b;
 }
 
 // E4M3 products on the matrix cores, one weight row at a time.  A 16x16x128
