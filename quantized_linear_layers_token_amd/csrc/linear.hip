@@ -166,11 +166,22 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         }
     }
 
-    v4u xr[SL];
+    // The lane's slices of the rounded token stay in registers, except for FP8
+    // rowwise rows longer than 8 KiB (XL): there each slice is read from the
+    // LDS copy where it is used and a wavefront takes one row, which keeps the
+    // kernel at or below 128 registers (four wavefronts per SIMD, every row of
+    // the launch in flight).  Measured over the Llama-3.1-8B decode step: FP8
+    // rowwise 1.392 -> 1.376 ms; the same form made int8 slower (1.372 ->
+    // 1.387 ms) and block FP8 slower (1.534 -> 1.556 ms on Qwen3-8B: 144
+    // registers, three wavefronts per SIMD).
+    constexpr bool XL = KC > 8 && V == VAR_FP8_ROW;
+    v4u xr[XL ? 1 : SL];
+    if constexpr (!XL) {
 #pragma unroll
-    for (int j = 0; j < SL; ++j) {
-        const int o = slot(j);
-        xr[j] = (o < k16) ? *reinterpret_cast<const v4u*>(xq + o * 16) : v4u{0, 0, 0, 0};
+        for (int j = 0; j < SL; ++j) {
+            const int o = slot(j);
+            xr[j] = (o < k16) ? *reinterpret_cast<const v4u*>(xq + o * 16) : v4u{0, 0, 0, 0};
+        }
     }
     const float s_tok = gsc[0];
 
@@ -187,11 +198,24 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     };
     float gx[NF];                  // block FP8: s_x of group l (and 64 + l)
     if constexpr (V == VAR_FP8_BLOCK) {
+        if constexpr (!XL) {
 #pragma unroll
-        for (int j = 0; j < SL; ++j) xr[j] = bperm(xr[j]);
+            for (int j = 0; j < SL; ++j) xr[j] = bperm(xr[j]);
+        }
 #pragma unroll
         for (int q = 0; q < NF; ++q) gx[q] = gsc[min(64 * q + lane, kbs - 1)];
     }
+
+    // the lane's token slice j (block FP8: the slice lane 4 (l % 16) + l / 16 loaded)
+    const int tlane = V == VAR_FP8_BLOCK ? 4 * (lane & 15) + (lane >> 4) : lane;
+    auto tok = [&](int j) -> v4u {
+        if constexpr (XL) {
+            const int o = j * kWave + tlane;
+            return (o < k16) ? *reinterpret_cast<const v4u*>(xq + o * 16) : v4u{0, 0, 0, 0};
+        } else {
+            return xr[j];
+        }
+    };
 
     // ---- stream the weight rows: the first group was loaded before the rounding
     auto process = [&](const v4u (&wr)[RL][SL], const uint32_t (&fw)[RL][NF], int n0) {
@@ -202,14 +226,14 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
             if constexpr (V == VAR_INT8) {
                 int a = 0;
 #pragma unroll
-                for (int j = 0; j < KC; ++j) a = dot16_i8(wr[r][j], xr[j], a);
+                for (int j = 0; j < KC; ++j) a = dot16_i8(wr[r][j], tok(j), a);
                 iacc[r] = wave_sum_i32(a);
             } else if constexpr (V == VAR_FP8_ROW) {
                 v4f c = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int q = 0; q < (SL + 1) / 2; ++q)
-                    c = mfma_e4m3(wr[r][2 * q], 2 * q + 1 < SL ? wr[r][2 * q + 1] : v4u{0, 0, 0, 0}, xr[2 * q],
-                                  2 * q + 1 < SL ? xr[2 * q + 1] : v4u{0, 0, 0, 0}, c);
+                    c = mfma_e4m3(wr[r][2 * q], 2 * q + 1 < SL ? wr[r][2 * q + 1] : v4u{0, 0, 0, 0}, tok(2 * q),
+                                  2 * q + 1 < SL ? tok(2 * q + 1) : v4u{0, 0, 0, 0}, c);
                 facc[r] = wave_sum_f32(mfma16_diag(c, lane));
             } else {
                 // one MFMA per KiB (half of its K slots zero): diagonal element i
@@ -222,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
                 float a = 0.0f;
 #pragma unroll
                 for (int q = 0; q < SL; ++q) {
-                    const v4f p = mfma_e4m3(bperm(wr[r][q]), v4u{0, 0, 0, 0}, xr[q], v4u{0, 0, 0, 0},
+                    const v4f p = mfma_e4m3(bperm(wr[r][q]), v4u{0, 0, 0, 0}, tok(q), v4u{0, 0, 0, 0},
                                             v4f{0.f, 0.f, 0.f, 0.f});
                     const int g = (8 * q + ((lane & 15) >> 1)) & 63;   // group 8 q + i / 2, in register q / 8
                     const float fg = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * g, __float_as_int(f[q / 8])));
@@ -272,9 +296,13 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         }
     };
     if (rb < re) process(cur, fsw, rb);
-    for (int n0 = rb + R; n0 < re; n0 += R) {
-        load_rows(cur, fsw, n0);
-        process(cur, fsw, n0);
+    // XL launches give every wavefront at most one row (or gate/up pair):
+    // without a second row in the loop the compiler keeps one row of weights
+    if constexpr (!XL) {
+        for (int n0 = rb + R; n0 < re; n0 += R) {
+            load_rows(cur, fsw, n0);
+            process(cur, fsw, n0);
+        }
     }
 }
 
@@ -301,13 +329,19 @@ void launch_kc(int R, int grid, hipStream_t st, const uint16_t* x, int K, const 
 // Launch shape (compared on one MI355X over the Llama-3.1-8B decode step):
 // rows of up to 4 KiB: one row per wavefront (the most workgroups, every load
 // issued at once); up to 8 KiB: two rows per wavefront read together; longer
-// rows: two rows per wavefront read one after the other (R = 1).
+// rows: two rows per wavefront read one after the other (R = 1), except FP8
+// rowwise: one row per wavefront, the token's slices read from LDS as they
+// are used (the kernel's long-row form).
 // SwiGLU mode: a wavefront reads one gate/up row pair at a time (two rows in
-// flight), one pair per wavefront for rows up to 4 KiB, else two in turn.
-void decode_launch_shape(int64_t ntot, int64_t K, int* R, int* grid) {
+// flight), one pair per wavefront for rows up to 4 KiB or past 8 KiB, else two
+// in turn.
+void decode_launch_shape(int variant, int64_t ntot, int64_t K, int* R, int* grid) {
     const int64_t kc = (K + 1023) / 1024;
     *R = (kc > 4 && kc <= 8) ? 2 : 1;
-    const int64_t rows = (kThreads / kWave) * (kc <= 4 ? 1 : 2);   // rows per workgroup
+    // one row per wavefront up to 4 KiB and, for FP8 rowwise, past 8 KiB (the
+    // kernel's long-row form handles exactly one), else two per wavefront
+    const bool one = kc <= 4 || (kc > 8 && variant == VAR_FP8_ROW);
+    const int64_t rows = (kThreads / kWave) * (one ? 1 : 2);   // rows per workgroup
     const int64_t g = (ntot + rows - 1) / rows;
     *grid = (int)(g < 1 ? 1 : g);
 }
@@ -316,7 +350,7 @@ hipError_t launch_linear_decode(int variant, const uint16_t* x, int64_t K, const
                                 uint8_t* qx, float* sx, hipStream_t st) {
     const int64_t ntot = mode == OUT_SWIGLU ? sa.start[1] : sa.start[sa.nseg];
     int R, grid;
-    decode_launch_shape(ntot, K, &R, &grid);
+    decode_launch_shape(variant, ntot, K, &R, &grid);
     const int64_t kc = (K + 1023) / 1024;
     const int k = (int)K;
 #define QLIN_DEC(VV)                                                              \
