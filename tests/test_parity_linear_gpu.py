@@ -74,6 +74,8 @@ CASES = [
     (1, 4096, [14336, 14336]),              # gate, up
     (1, 14336, [4096]),                     # down
     (1, 12288, [4096]),                     # Qwen3 down
+    (1, 9216, [384, 256]),                  # rows past 8 KiB, ragged last KiB slots (long-row form)
+    (1, 16384, [256, 128]),                 # the one-launch limit
     (1, 1152, [256, 384, 128, 640]),        # four segments, ragged widths
     (3, 1024, [256, 128]),                  # small-M kernel rounding the tokens itself
     (40, 512, [384]),                       # staged path (tiled GEMM)
