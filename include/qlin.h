@@ -50,7 +50,7 @@ extern "C" {
 /* Same type as HIP's own hipStream_t. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define QLIN_ABI_VERSION 2
+#define QLIN_ABI_VERSION 3
 #define QLIN_MAX_K  131072          /* 127 * 128 * K stays below 2^31 */
 #define QLIN_MAX_MN (1 << 24)
 
@@ -282,6 +282,45 @@ qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M,
                                const void* gate_q_w, const uint16_t* gate_s_w,
                                const void* up_q_w, const uint16_t* up_s_w, int64_t I,
                                uint16_t* h, void* q_x, float* s_x, hipStream_t stream);
+
+/* Weights in the matrix-core operand order ("packed"), for long inputs.
+ * The pages give the product only for row-major codes (W8A8 model card,
+ * "Loading": longer inputs are rounded per row and multiplied in int8 with
+ * int32 sums); this is the same product with the weight bytes reordered so
+ * that each wavefront of the tiled kernel loads its weight rows straight into
+ * the matrix-core operand registers, 1 KB contiguous per load, and only the
+ * tokens pass through LDS.  q_w [N, K] is cut into blocks of 32 rows and
+ * K-slices of S bytes (S = 32 for W8A8, 64 for FP8_ROWWISE); with H = S / 32:
+ *   packed[((rb * (K / S) + s) * H + h) * 1024 + 16 l + b]
+ *     = q_w[32 rb + l % 32][S s + (S / 2) (l / 32) + 16 h + b],   l < 64, b < 16
+ * (a permutation of the N * K bytes).
+ *
+ * qlin_pack_weights: q_w row-major [N, K] codes in, q_w_packed [N * K bytes]
+ * out (caller-owned device memory, 16-byte aligned, not overlapping q_w).
+ * scheme QLIN_SCHEME_W8A8 or QLIN_SCHEME_FP8_ROWWISE (FP8_BLOCK:
+ * QLIN_ERR_UNSUPPORTED); N % 128 == 0 and K % 128 == 0 (else QLIN_ERR_SHAPE);
+ * N == 0 is a no-op.  One launch on stream; the scales are not touched (s_w
+ * stays per row, in row order). */
+qlin_status qlin_pack_weights(qlin_scheme scheme, const void* q_w, int64_t N, int64_t K, void* q_w_packed,
+                              hipStream_t stream);
+
+/* qlin_linear on packed weights: every segments[i].q_w is the qlin_pack_weights
+ * output of that segment's codes (s_w and y as for qlin_linear).  Same results
+ * as qlin_linear bit for bit for W8A8 (same int32 sums, same epilogue order);
+ * FP8_ROWWISE within the tolerance of the FP8 paths (f32 sums, another
+ * summation order).  For long inputs only: M >= 33 (smaller M:
+ * QLIN_ERR_UNSUPPORTED, the one-row and small-M kernels read row-major
+ * weights), every segment's n % 128 == 0 and K % 128 == 0 (QLIN_ERR_SHAPE),
+ * scheme W8A8 or FP8_ROWWISE (FP8_BLOCK: QLIN_ERR_UNSUPPORTED); q_x / s_x are
+ * required staging buffers as in the staged qlin_linear: one quantizer launch,
+ * then one tiled launch over every segment (128 weight rows x 64 or 128 tokens
+ * per tile).  Validation, aliasing rules and error behaviour as qlin_linear.
+ * Packing pays on projections whose outputs give each CU at most a 128 x 128
+ * tile (q/k/v, o and down of an 8B model at 512-1024 tokens); the wide gate/up
+ * projection runs faster row-major on the 256 x 256 tiles of qlin_linear. */
+qlin_status qlin_linear_packed(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                               const qlin_segment* segments, int32_t nseg, qlin_out out,
+                               void* q_x, float* s_x, hipStream_t stream);
 
 /* Staging capacity of qlin_linear_noalloc: activation codes (M * K bytes) and
  * activation scales (M or M * K/128 floats). */

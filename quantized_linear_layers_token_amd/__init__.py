@@ -25,7 +25,7 @@ PATH_LARGE_256X128, PATH_LARGE_128X128, PATH_LARGE_128X64, PATH_LARGE_128X256 = 
 PATH_LARGE_128X128_K2, PATH_LARGE_128X64_K2 = 8, 9
 PATH_LARGE_256X256_W8 = 10   # int8 and FP8 rowwise only
 PATH_LARGE_256X256 = 11      # int8 and FP8 rowwise only
-ABI_VERSION = 2
+ABI_VERSION = 3
 NOALLOC_MAX_CODE_BYTES = 16 << 20    # staging capacity of qlin_linear_noalloc
 NOALLOC_MAX_SCALES = 1 << 20
 MAX_K = 131072
@@ -49,6 +49,8 @@ SIGNATURES = {
     "qlin_linear_weight_only": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P]),
     "qlin_linear_swiglu": (_S, [_S, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P, _P, _P]),
     "qlin_linear_noalloc": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P]),
+    "qlin_pack_weights": (_S, [_S, _P, _I64, _I64, _P, _P]),
+    "qlin_linear_packed": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P, _P, _P]),
     "qlin_status_string": (ctypes.c_char_p, [_S]),
     "qlin_abi_version": (_S, []),
     "qlin_last_hip_error": (_S, []),
@@ -254,6 +256,27 @@ def qlin_linear(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=No
     arr = segments_array(segments)
     _check(_lib.qlin_linear(scheme, _ptr(x), M, K, arr, len(segments), out, _ptr(q_x), _ptr(s_x),
                             _stream(stream)), "qlin_linear")
+
+
+def qlin_pack_weights(scheme, q_w, q_w_packed, stream=None):
+    """Reorders q_w [N, K] (1-byte codes, row-major) into the matrix-core
+    operand order of qlin_linear_packed, written to q_w_packed (N * K bytes,
+    e.g. a tensor like q_w).  W8A8 and FP8 rowwise; N and K multiples of 128."""
+    N, K = _dims2(q_w, "q_w", 1)
+    _args(("q_w_packed", q_w_packed, N * K, 1), ("q_w", q_w, 0, None))
+    _check(_lib.qlin_pack_weights(scheme, _ptr(q_w), N, K, _ptr(q_w_packed), _stream(stream)), "qlin_pack_weights")
+
+
+def qlin_linear_packed(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=None):
+    """qlin_linear for M >= 33 with every segment's q_w [n, K] in the packed
+    order that qlin_pack_weights writes (s_w and y as for qlin_linear);
+    q_x / s_x staging required."""
+    M, K = _dims2(x, "x", 2)
+    _args(*_segment_args(scheme, M, K, segments, out), ("q_x", q_x, M * K, 1),
+          ("s_x", s_x, 4 * _sx_count(False, M, K), 4), ("x", x, 0, None))
+    arr = segments_array(segments)
+    _check(_lib.qlin_linear_packed(scheme, _ptr(x), M, K, arr, len(segments), out, _ptr(q_x), _ptr(s_x),
+                                   _stream(stream)), "qlin_linear_packed")
 
 
 def qlin_linear_noalloc(scheme, x, segments, out=OUT_BF16, stream=None):

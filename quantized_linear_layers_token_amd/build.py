@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlin.so")
 
 ARCH = "gfx950"
-SOURCES = ["quant_act.hip", "gemv.hip", "gemm_small.hip", "gemm_large.hip", "linear.hip", "linear_tokens.hip", "weight_only.hip",
+SOURCES = ["quant_act.hip", "gemv.hip", "gemm_small.hip", "gemm_large.hip", "gemm_packed.hip", "linear.hip", "linear_tokens.hip", "weight_only.hip",
            "noalloc.hip",
            "qlin_api.hip"]
 HEADERS = ["qlin_device.h", "qlin_internal.h", "qlin_round.h", "qlin_rows.h"]

@@ -234,6 +234,53 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
 }
 
 
+qlin_status qlin_pack_weights(qlin_scheme scheme, const void* q_w, int64_t N, int64_t K, void* q_w_packed,
+                              hipStream_t stream) {
+    if (scheme != QLIN_SCHEME_W8A8 && scheme != QLIN_SCHEME_FP8_ROWWISE) return QLIN_ERR_UNSUPPORTED;
+    if (!valid_mn(N) || !valid_k(K) || (N % 128) != 0 || (K % 128) != 0) return QLIN_ERR_SHAPE;
+    if (N == 0) return QLIN_OK;
+    if (!q_w || !q_w_packed) return QLIN_ERR_NULL;
+    if (!aligned(q_w, 16) || !aligned(q_w_packed, 16)) return QLIN_ERR_ALIGN;
+    if (overlap(rng(q_w, N * K), rng(q_w_packed, N * K))) return QLIN_ERR_ALIAS;
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8 : qlin::VAR_FP8_ROW;
+    return hip_status(qlin::launch_pack_weights(variant, static_cast<const uint8_t*>(q_w), N, K,
+                                                static_cast<uint8_t*>(q_w_packed), stream));
+}
+
+qlin_status qlin_linear_packed(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                               const qlin_segment* segments, int32_t nseg, qlin_out out, void* q_x, float* s_x,
+                               hipStream_t stream) {
+    if (scheme != QLIN_SCHEME_W8A8 && scheme != QLIN_SCHEME_FP8_ROWWISE) return QLIN_ERR_UNSUPPORTED;
+    bool noop = false;
+    // the staged form's checks (staging buffers required)
+    const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, q_x, s_x, false, &noop);
+    if (st != QLIN_OK || noop) return st;
+    if ((K % 128) != 0) return QLIN_ERR_SHAPE;
+    for (int i = 0; i < nseg; ++i)
+        if ((segments[i].n % 128) != 0) return QLIN_ERR_SHAPE;
+    if (M < 33) return QLIN_ERR_UNSUPPORTED;
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8 : qlin::VAR_FP8_ROW;
+    qlin::SegmentArgs sa{};
+    int n = 0, k = 0;
+    for (int i = 0; i < nseg; ++i) {
+        if (segments[i].n == 0) continue;
+        sa.w[k] = static_cast<const uint8_t*>(segments[i].q_w);
+        sa.sw[k] = segments[i].s_w;
+        sa.y[k] = segments[i].y;
+        sa.start[k] = n;
+        n += (int)segments[i].n;
+        ++k;
+    }
+    sa.nseg = k;
+    for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
+    hipError_t e;
+    if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);
+    else e = qlin::launch_quant_fp8(x, M, K, 0, static_cast<uint8_t*>(q_x), s_x, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(qlin::launch_gemm_packed(variant, static_cast<const uint8_t*>(q_x), s_x, sa, M, K, (int)out,
+                                               stream));
+}
+
 qlin_status qlin_linear_weight_only(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
                                     const qlin_segment* segments, int32_t nseg, qlin_out out, hipStream_t stream) {
     if (out == QLIN_OUT_I32) return QLIN_ERR_UNSUPPORTED;

@@ -48,6 +48,11 @@ hipError_t launch_gemm_small_fused(int, const uint16_t*, int64_t, int64_t, const
                                    hipStream_t) {
     return reached();
 }
+hipError_t launch_gemm_packed(int, const uint8_t*, const float*, const SegmentArgs&, int64_t, int64_t, int,
+                              hipStream_t) {
+    return reached();
+}
+hipError_t launch_pack_weights(int, const uint8_t*, int64_t, int64_t, uint8_t*, hipStream_t) { return reached(); }
 hipError_t launch_weight_only(int, const uint16_t*, int64_t, int64_t, const SegmentArgs&, int, hipStream_t) {
     return reached();
 }

@@ -28,6 +28,8 @@ SIG = {
     "qlin_gemm_fp8_rowwise_ex": [P, P, P, P, P, I64, I64, I64, S, S, P],
     "qlin_gemm_fp8_block_ex": [P, P, P, P, P, I64, I64, I64, S, S, P],
     "qlin_linear": [S, P, I64, I64, P, I32, S, P, P, P],
+    "qlin_linear_packed": [S, P, I64, I64, P, I32, S, P, P, P],
+    "qlin_pack_weights": [S, P, I64, I64, P, P],
     "qlin_linear_weight_only": [S, P, I64, I64, P, I32, S, P],
     "qlin_linear_swiglu": [S, P, I64, I64, P, P, P, P, I64, P, P, P, P],
 }
@@ -113,6 +115,14 @@ assert call("qlin_linear_swiglu", 0, x, 1, 256, A + 0x1000000, A + 0x2000000, A 
             A + 0x6000000, None, None, None) == OK
 assert call("qlin_linear_swiglu", 2, x, 1, 256, A + 0x1000000, A + 0x2000000, A + 0x4000000, A + 0x5000000, 100,
             A + 0x6000000, None, None, None) == SHAPE
+wide = segs((A + 0x1000000, A + 0x2000000, A + 0x3000000, 128), (A + 0x4000000, A + 0x5000000, A + 0x6000000, 256))
+assert call("qlin_linear_packed", 0, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == OK
+assert call("qlin_linear_packed", 0, x, 32, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == UNSUP
+assert call("qlin_linear_packed", 0, x, 64, 256, three, 3, 0, A + 0xA000000, A + 0xB000000, None) == SHAPE
+assert call("qlin_linear_packed", 2, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == UNSUP
+assert call("qlin_pack_weights", 1, A, 256, 384, A + 0x1000000, None) == OK
+assert call("qlin_pack_weights", 1, A, 256, 384, A + 0x100, None) == ALIAS
+assert call("qlin_pack_weights", 0, A, 200, 384, A + 0x1000000, None) == SHAPE
 assert call("qlin_quant_act_fp8", x, 4, 256, 64, A + 0x1000000, A + 0x2000000, None) == SHAPE
 assert call("qlin_quant_act_fp8", x, 4, 200, 128, A + 0x1000000, A + 0x2000000, None) == SHAPE
 assert call("qlin_quant_act_int8", x, 4, 256, x + 256, A + 0x2000000, None) == ALIAS
@@ -140,7 +150,7 @@ def size():
 
 
 for it in range(20000):
-    fn = rng.randrange(7)
+    fn = rng.randrange(8)
     M, N, K = size(), size(), rng.choice([16, 128, 256, 4096, 14336, 250, 0, -16, 131072, 131200])
     out, path = rng.choice([0, 1, 2, 3, -1]), rng.choice(list(range(0, 12)) + [-1, 12, 99])
     scheme = rng.choice([0, 1, 2, 3, -1])
@@ -160,9 +170,12 @@ for it in range(20000):
         # the count passed is the array's, or one the library must refuse before reading (0, 5, -1)
         cnt = rng.choice([nseg, nseg, 0, 5, -1]) if nseg else rng.choice([0, 5, -1])
         if fn == 4:
-            call("qlin_linear", scheme, ptr(), M, K, arr, cnt, out, ptr(), ptr(), None)
+            call(rng.choice(["qlin_linear", "qlin_linear_packed"]), scheme, ptr(), M, K, arr, cnt, out, ptr(), ptr(),
+                 None)
         else:
             call("qlin_linear_weight_only", scheme, ptr(), M, K, arr, cnt, out, None)
+    elif fn == 7:
+        call("qlin_pack_weights", scheme, ptr(), N, K, ptr(), None)
     else:
         call("qlin_linear_swiglu", scheme, ptr(), M, K, ptr(), ptr(), ptr(), ptr(), size(), ptr(), ptr(), ptr(), None)
 

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libqlin.so"
         assert n in Q.SIGNATURES, f"{n} has no binding signature"
@@ -212,6 +212,38 @@ def test_linear_swiglu_validation():
     assert sg(0, x, 1, 256, gq, gs, uq, us, 128, uq + 256, None, None, None) == Q.QLIN_ERR_ALIAS  # h in up
     assert sg(0, x, 1, 256, gq, gs, uq, us, 128, gs, None, None, None) == Q.QLIN_ERR_ALIAS        # h on gate scales
     assert sg(0, x, 4, 256, gq, gs, uq, us, 128, qx, qx, sx, None) == Q.QLIN_ERR_ALIAS            # h on staging
+
+
+def test_pack_weights_validation():
+    pk = L.qlin_pack_weights
+    w, p = A, A + 0x1000000
+    assert pk(2, w, 256, 384, p, None) == Q.QLIN_ERR_UNSUPPORTED      # block scheme: not packed
+    assert pk(9, w, 256, 384, p, None) == Q.QLIN_ERR_UNSUPPORTED
+    assert pk(0, w, 200, 384, p, None) == Q.QLIN_ERR_SHAPE            # N % 128
+    assert pk(1, w, 256, 400, p, None) == Q.QLIN_ERR_SHAPE            # K % 128
+    assert pk(0, w, -128, 384, p, None) == Q.QLIN_ERR_SHAPE
+    assert pk(0, w, 0, 384, p, None) == Q.QLIN_OK                     # no rows: no-op
+    assert pk(0, None, 256, 384, p, None) == Q.QLIN_ERR_NULL
+    assert pk(0, w, 256, 384, None, None) == Q.QLIN_ERR_NULL
+    assert pk(0, w + 8, 256, 384, p, None) == Q.QLIN_ERR_ALIGN
+    assert pk(0, w, 256, 384, w + 256 * 384 - 16, None) == Q.QLIN_ERR_ALIAS
+
+
+def test_linear_packed_validation():
+    Seg = Q.QlinSegment
+    x, qx, sx = A, A + 0xA000000, A + 0xB000000
+    segs = (Seg * 2)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 128),
+                     Seg(A + 0x4000000, A + 0x5000000, A + 0x6000000, 256))
+    odd = (Seg * 1)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 64))
+    lp = L.qlin_linear_packed
+    assert lp(2, x, 64, 256, segs, 2, 0, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED   # block scheme
+    assert lp(0, x, 32, 256, segs, 2, 0, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED   # M <= 32: row-major kernels
+    assert lp(0, x, 64, 256, odd, 1, 0, qx, sx, None) == Q.QLIN_ERR_SHAPE          # n % 128
+    assert lp(0, x, 64, 272, segs, 2, 0, qx, sx, None) == Q.QLIN_ERR_SHAPE         # K % 128
+    assert lp(0, x, 64, 256, segs, 2, 0, None, None, None) == Q.QLIN_ERR_NULL      # staging required
+    assert lp(1, x, 64, 256, segs, 2, Q.OUT_I32, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED
+    assert lp(0, x, 0, 256, segs, 2, 0, qx, sx, None) == Q.QLIN_OK                 # M == 0
+    assert lp(0, x, 64, 256, segs, 2, 0, A + 0x1000000 + 64, sx, None) == Q.QLIN_ERR_ALIAS   # q_x in q_w
 
 
 def test_library_has_no_unresolved_internal_symbols():

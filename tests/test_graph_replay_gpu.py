@@ -1,7 +1,8 @@
 """The library's calls captured in one HIP graph and replayed: every launch
 form of qlin_linear / qlin_linear_swiglu (one token; two tokens; four tokens
 rounded in the small-M kernel; quantizer + small-M kernel; quantizer + tiled
-GEMM, including its 8-wavefront 256 x 256 tile) must reproduce the eager results bit for bit on every replay, with
+GEMM, including its 8-wavefront 256 x 256 tile; quantizer + the packed-weight
+GEMM on both token-tile widths) must reproduce the eager results bit for bit on every replay, with
 eager work (output poisoning, another library call) between the replays."""
 import numpy as np
 import pytest
@@ -48,6 +49,21 @@ def build(torch):
     sx = empty(torch, (257,), torch.float32)
     outs += [qx, sx]
     calls.append(lambda x=x, segs=segs, qx=qx, sx=sx: Q().qlin_linear(FP8R, x, segs, q_x=qx, s_x=sx))
+    # packed weights: W8A8 on 64-token tiles, FP8 rowwise on 128-token tiles
+    for i, (scheme, M, K, ns) in enumerate([(W8A8, 100, 512, [256, 128]), (FP8R, 300, 256, [4096, 4096])]):
+        x = dev(W.x_bf16(9960 + i, M, K))
+        segs = []
+        for j, n in enumerate(ns):
+            qw = dev(W.w_int8(9962 + 2 * i + j, n, K) if scheme == W8A8 else W.w_e4m3(9962 + 2 * i + j, n, K))
+            pw = torch.empty_like(qw)
+            Q().qlin_pack_weights(scheme, qw, pw)
+            y = empty(torch, (M, n), torch.int16)
+            segs.append((pw, dev(W.scale_bf16(9966 + 2 * i + j, (n,))), y))
+            outs.append(y)
+        qx = empty(torch, (M, K), torch.uint8)
+        sx = empty(torch, (M,), torch.float32)
+        outs += [qx, sx]
+        calls.append(lambda s=scheme, x=x, segs=segs, qx=qx, sx=sx: Q().qlin_linear_packed(s, x, segs, q_x=qx, s_x=sx))
     for i, (M, K) in enumerate([(1, 4096), (4, 1024), (40, 512)]):
         x = dev(W.x_bf16(9980 + i, M, K))
         gate = (dev(W.w_int8(9985 + i, 256, K)), dev(W.scale_bf16(9988 + i, 256, 1e-4, 5e-4)))

@@ -24,7 +24,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "quantized_linear_layers_token_amd", "csrc")
-KERNELS = ["gemm_large.hip", "gemm_small.hip", "linear.hip", "linear_tokens.hip", "weight_only.hip", "gemv.hip",
+KERNELS = ["gemm_large.hip", "gemm_packed.hip", "gemm_small.hip", "linear.hip", "linear_tokens.hip", "weight_only.hip", "gemv.hip",
            "quant_act.hip"]
 
 PASSES = {

@@ -1,0 +1,190 @@
+"""GPU parity of the packed-weight path: qlin_pack_weights against the layout
+definition (a numpy reshape/transpose of the row-major codes, written from the
+layout formula in include/qlin.h), and qlin_linear_packed against the CPU
+oracle -- W8A8 bit for bit (same int32 sums, same f32 epilogue order; the
+int32 accumulator output exactly), FP8 rowwise within the FP8 tolerance --
+on 64- and 128-token tiles, ragged token tails, several segments, and the
+q/k/v, o and down shapes of an 8B model at 512 tokens."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_helpers import assert_within_tol, dev, empty, host, torch_mod
+
+pytestmark = pytest.mark.gpu
+BF16, I32, F32 = 0, 1, 2
+W8A8, FP8R = 0, 1
+
+
+def Q():
+    import quantized_linear_layers_token_amd as q
+    return q
+
+
+def packed_reference(w: np.ndarray, S: int) -> np.ndarray:
+    """packed[((rb * (K/S) + s) * H + h) * 1024 + 16 l + b] =
+    w[32 rb + l % 32][S s + (S/2)(l / 32) + 16 h + b], H = S / 32, as a reshape."""
+    N, K = w.shape
+    H = S // 32
+    # axes of w: rb, r (= l % 32), s, half (= l / 32), h, b
+    v = w.reshape(N // 32, 32, K // S, 2, H, 16)
+    # packed order: rb, s, h, half, r, b   (l = 32 half + r)
+    return np.ascontiguousarray(v.transpose(0, 2, 4, 3, 1, 5)).reshape(-1)
+
+
+def test_packed_reference_is_a_permutation_with_the_stated_entries():
+    # the reshape above against the formula, entry by entry, on a small case
+    rng = np.random.default_rng(5)
+    for S in (32, 64):
+        N, K = 64, 128
+        w = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+        p = packed_reference(w, S)
+        H = S // 32
+        for _ in range(2000):
+            rb, s, h = rng.integers(0, N // 32), rng.integers(0, K // S), rng.integers(0, H)
+            l, b = rng.integers(0, 64), rng.integers(0, 16)
+            got = p[((rb * (K // S) + s) * H + h) * 1024 + 16 * l + b]
+            assert got == w[32 * rb + l % 32, S * s + (S // 2) * (l // 32) + 16 * h + b]
+        assert np.array_equal(np.sort(p), np.sort(w.reshape(-1)))
+
+
+@pytest.mark.parametrize("scheme,S", [(W8A8, 32), (FP8R, 64)])
+@pytest.mark.parametrize("N,K", [(128, 128), (384, 1024), (256, 14336)])
+def test_pack_weights_layout(scheme, S, N, K):
+    torch = torch_mod()
+    w = W.w_int8(8000 + N, N, K).view(np.uint8) if scheme == W8A8 else W.w_e4m3(8000 + N, N, K)
+    p = empty(torch, (N * K + 64,), torch.uint8, fill=0xA5)
+    Q().qlin_pack_weights(scheme, dev(w), p[:N * K])
+    got = host(p)
+    assert (got[N * K:] == 0xA5).all(), "guard band overwritten"
+    assert np.array_equal(got[:N * K], packed_reference(np.ascontiguousarray(w), S))
+
+
+def packed_segments(scheme, seed, ns, K):
+    """[(row-major codes, scales, packed device codes)] for each width."""
+    torch = torch_mod()
+    out = []
+    for i, n in enumerate(ns):
+        qw = W.w_int8(seed + 10 * i, n, K) if scheme == W8A8 else W.w_e4m3(seed + 10 * i, n, K)
+        sw = W.scale_bf16(seed + 10 * i + 1, (n,))
+        pw = empty(torch, (n, K), torch.uint8)
+        Q().qlin_pack_weights(scheme, dev(qw), pw)
+        out.append((qw, sw, pw))
+    return out
+
+
+def run_packed(scheme, x, segs, out):
+    torch = torch_mod()
+    M, K = x.shape
+    esz = 2 if out == BF16 else 4
+    ys = [empty(torch, (M * qw.shape[0] * esz + 64,), torch.uint8, fill=0xFF) for qw, _, _ in segs]
+    qx = empty(torch, (M, K), torch.uint8, fill=0x55)
+    sx = empty(torch, (M,), torch.float32, fill=0x55)
+    Q().qlin_linear_packed(scheme, dev(x), [(pw, dev(sw), y) for (_, sw, pw), y in zip(segs, ys)], out=out,
+                           q_x=qx, s_x=sx)
+    res = []
+    for (qw, _, _), y in zip(segs, ys):
+        raw = host(y)
+        n = qw.shape[0]
+        assert (raw[M * n * esz:] == 0xFF).all(), "guard band overwritten"
+        res.append(raw[:M * n * esz].view({BF16: np.uint16, I32: np.int32, F32: np.float32}[out]).reshape(M, n))
+    return res
+
+
+CASES = [
+    # (M, K, segment widths): token tiles of 64 unless tiles x panels >= 192
+    (33, 128, [128]),                       # smallest M, one tile, 31 rows past M
+    (64, 256, [128, 256]),                  # exactly one tile, two segments
+    (200, 1024, [384, 128]),                # ragged last tile (8 tokens)
+    (130, 512, [1024, 256, 256]),           # q/k/v-shaped segments, 2 tokens in the last tile
+    (300, 256, [4096, 4096]),               # 128-token tiles (3 x 64 panels), ragged 44
+    (97, 4096, [640, 128, 512, 256]),       # four segments, long K
+]
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R])
+@pytest.mark.parametrize("M,K,ns", CASES)
+def test_linear_packed_matches_oracle(scheme, M, K, ns):
+    x = W.x_bf16(8100 + M + K + len(ns), M, K)
+    segs = packed_segments(scheme, 8200 + K, ns, K)
+    qx_ref, sx_ref = O.quant_act_int8(x) if scheme == W8A8 else O.quant_act_fp8(x, 0)
+    ys = run_packed(scheme, x, segs, BF16)
+    for (qw, sw, _), y in zip(segs, ys):
+        if scheme == W8A8:
+            acc = O.contract_int8(qx_ref, qw)
+            assert np.array_equal(y, O.epilogue_f32_order(acc, sx_ref, sw))
+            assert_within_tol(y, O.rescale_rowwise(acc, sx_ref, sw), "packed W8A8")
+        else:
+            assert_within_tol(y, O.rescale_rowwise(O.contract_e4m3(qx_ref, qw), sx_ref, sw), "packed FP8 rowwise")
+
+
+@pytest.mark.parametrize("M", [100, 300])
+def test_linear_packed_int8_accumulator_and_f32_exact(M):
+    K, ns = 512, [4096, 4096] if M == 300 else [256, 384]
+    x = W.x_bf16(8300 + M, M, K)
+    segs = packed_segments(W8A8, 8301, ns, K)
+    qx_ref, sx_ref = O.quant_act_int8(x)
+    acc_ys = run_packed(W8A8, x, segs, I32)
+    f32_ys = run_packed(W8A8, x, segs, F32)
+    for (qw, sw, _), ya, yf in zip(segs, acc_ys, f32_ys):
+        acc = O.contract_int8(qx_ref, qw)
+        assert np.array_equal(ya, acc)
+        assert_within_tol(yf, O.rescale_rowwise(acc, sx_ref, sw), "packed W8A8 f32", f32=True)
+
+
+def test_linear_packed_fp8_f32_output():
+    M, K = 150, 1024
+    x = W.x_bf16(8400, M, K)
+    segs = packed_segments(FP8R, 8401, [256, 512], K)
+    qx_ref, sx_ref = O.quant_act_fp8(x, 0)
+    for (qw, sw, _), y in zip(segs, run_packed(FP8R, x, segs, F32)):
+        assert_within_tol(y, O.rescale_rowwise(O.contract_e4m3(qx_ref, qw), sx_ref, sw), "packed FP8 f32", f32=True)
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R])
+@pytest.mark.parametrize("name,K,ns", [("qkv", 4096, [4096, 1024, 1024]), ("o", 4096, [4096]),
+                                       ("down", 14336, [4096])])
+def test_linear_packed_llama8b_512_tokens(scheme, name, K, ns):
+    # the projections the packed path serves, at the prefill size it is timed on
+    M = 512
+    x = W.x_bf16(8500 + K, M, K)
+    segs = packed_segments(scheme, 8600 + K, ns, K)
+    qx_ref, sx_ref = O.quant_act_int8(x) if scheme == W8A8 else O.quant_act_fp8(x, 0)
+    ys = run_packed(scheme, x, segs, BF16)
+    for (qw, sw, _), y in zip(segs, ys):
+        if scheme == W8A8:
+            assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw)), name
+        else:
+            assert_within_tol(y, O.rescale_rowwise(O.contract_e4m3(qx_ref, qw), sx_ref, sw), name)
+
+
+def test_linear_packed_matches_row_major_path():
+    # same int8 call through qlin_linear (row-major tiled GEMM) and qlin_linear_packed
+    torch = torch_mod()
+    M, K, n = 257, 2048, 768
+    x = dev(W.x_bf16(8700, M, K))
+    qw = dev(W.w_int8(8701, n, K))
+    sw = dev(W.scale_bf16(8702, (n,)))
+    pw = torch.empty_like(qw)
+    Q().qlin_pack_weights(W8A8, qw, pw)
+    qx, sx = empty(torch, (M, K), torch.uint8), empty(torch, (M,), torch.float32)
+    y1, y2 = empty(torch, (M, n), torch.int16), empty(torch, (M, n), torch.int16)
+    Q().qlin_linear(W8A8, x, [(qw, sw, y1)], q_x=qx, s_x=sx)
+    Q().qlin_linear_packed(W8A8, x, [(pw, sw, y2)], q_x=qx, s_x=sx)
+    assert torch.equal(y1, y2)
+
+
+def test_linear_packed_refuses_small_m_and_block_scheme():
+    torch = torch_mod()
+    K, n = 256, 128
+    x = dev(W.x_bf16(8800, 32, K))
+    pw = dev(W.w_int8(8801, n, K))
+    sw = dev(W.scale_bf16(8802, (n,)))
+    y = empty(torch, (32, n), torch.int16, fill=0x3C)
+    qx, sx = empty(torch, (32, K), torch.uint8), empty(torch, (32,), torch.float32)
+    with pytest.raises(Q().QlinError):
+        Q().qlin_linear_packed(W8A8, x, [(pw, sw, y)], q_x=qx, s_x=sx)
+    with pytest.raises(Q().QlinError):
+        Q().qlin_pack_weights(2, pw, torch.empty_like(pw))
+    assert (host(y).view(np.uint8) == 0x3C).all()      # nothing launched
