@@ -146,45 +146,49 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
 #pragma unroll
     for (int i = 0; i < TM; ++i) acc[i] = Acc{};
 
-    auto compute = [&](auto bi) {
-        const v4u(&ar)[4] = aset(bi);
+    // Token fragments: sub-step u of a stage is one MFMA K slice (int8: 4 of
+    // 32 bytes, E4M3: 2 of 64 bytes); a wavefront reads the TM fragments of
+    // sub-step u + 1 from LDS while it multiplies those of u (two sets; the
+    // scheduling barriers keep the compiler from sinking the reads next to
+    // their MFMAs, which would expose the LDS latency at every pair).
+    constexpr int NSUB = V == VAR_INT8 ? 4 : 2;
+    typedef typename std::conditional<V == VAR_INT8, v4i, v8i>::type BFrag;
+    BFrag bq[2][TM];
+    auto rdsub = [&](auto bi, int p, int sub) {
         const uint8_t* base = buf(bi);
         auto rdq = [&](int r, int c) { return *reinterpret_cast<const v4i*>(base + r * 128 + ((c ^ pswz(r)) << 4)); };
-        if constexpr (V == VAR_INT8) {
-            v4i bq[2][TM];
-            auto rd = [&](int p, int sub) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) bq[p][i] = rdq(i * 32 + (lane & 31), 2 * sub + half);
-            };
-            rd(0, 0);
-#pragma unroll
-            for (int sub = 0; sub < 4; ++sub) {
-                if (sub + 1 < 4) rd((sub + 1) & 1, sub + 1);
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, ar[sub]), bq[sub & 1][i], acc[i],
-                                                                   0, 0, 0);
+        for (int i = 0; i < TM; ++i) {
+            const int r = i * 32 + (lane & 31);
+            if constexpr (V == VAR_INT8) {
+                bq[p][i] = rdq(r, 2 * sub + half);
+            } else {
+                const v4i lo = rdq(r, 4 * sub + 2 * half), hi = rdq(r, 4 * sub + 2 * half + 1);
+                bq[p][i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             }
-        } else {
-            v8i bq[2][TM];
-            auto rd = [&](int p, int sub) {
+        }
+    };
+    auto mfsub = [&](auto bi, int p, int sub) {
+        const v4u(&ar)[4] = aset(bi);
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int r = i * 32 + (lane & 31);
-                    const v4i lo = rdq(r, 4 * sub + 2 * half), hi = rdq(r, 4 * sub + 2 * half + 1);
-                    bq[p][i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                }
-            };
-            rd(0, 0);
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                if (sub + 1 < 2) rd(1, 1);
+        for (int i = 0; i < TM; ++i) {
+            if constexpr (V == VAR_INT8) {
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, ar[sub]), bq[p][i], acc[i], 0, 0, 0);
+            } else {
                 const v4u lo = ar[2 * sub], hi = ar[2 * sub + 1];
                 const v8i a = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq[sub][i], acc[i], 0, 0, 0, 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq[p][i], acc[i], 0, 0, 0, 0, 0, 0);
             }
+        }
+    };
+    // sub-step 0's reads were issued before the stage's loads (see step)
+    auto compute = [&](auto bi) {
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            if (sub + 1 < NSUB) rdsub(bi, (sub + 1) & 1, sub + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfsub(bi, sub & 1, sub);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -225,6 +229,8 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WIMM);
         asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        rdsub(bi, 0, 0);                         // in flight while the next stage's loads issue
         __builtin_amdgcn_sched_barrier(0);
         issue(PIC<(v + 3) & 3>{}, gs(kt + 3));
         __builtin_amdgcn_sched_barrier(0);
