@@ -297,7 +297,9 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
     prod = Launcher(Q, torch)
     fused = Launcher(Q, torch)
     swiglu = Launcher(Q, torch)     # fused, with gate/up as one SwiGLU launch
-    packed = Launcher(Q, torch) if variant != "fp8_block" else None
+    packed = Launcher(Q, torch)     # swiglu's calls with q/k/v, o and down on packed weights
+    packed_all = Launcher(Q, torch)  # fused's calls, every projection on packed weights
+    packed.outputs = []
     scheme = {"int8": Q.SCHEME_W8A8, "fp8_row": Q.SCHEME_FP8_ROWWISE, "fp8_block": Q.SCHEME_FP8_BLOCK}[variant]
     gen = torch.Generator(device=dev)
     ops = 0
@@ -335,22 +337,21 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
                 ops += 2 * M * N * K
             # the group as one call: quantization + one GEMM launch over its segments
             fused.linear(scheme, x, segs, qx=q, sx=s)
+            psegs = []
+            for qw, sw, y in segs:
+                pw = torch.empty_like(qw)
+                Q.qlin_pack_weights(scheme, qw, pw)
+                keep.append(pw)
+                psegs.append((pw, sw, y))
+            packed_all.linear_packed(scheme, x, psegs, qx=q, sx=s)
             if group == ("gate", "up"):
                 swiglu.linear_swiglu(scheme, x, segs[0][:2], segs[1][:2], segs[0][2], qx=q, sx=s)
-                if packed is not None:
-                    packed.linear_swiglu(scheme, x, segs[0][:2], segs[1][:2], segs[0][2], qx=q, sx=s)
+                packed.linear_swiglu(scheme, x, segs[0][:2], segs[1][:2], segs[0][2], qx=q, sx=s)
             else:
                 swiglu.linear(scheme, x, segs, qx=q, sx=s)
-                if packed is not None:
-                    psegs = []
-                    for qw, sw, y in segs:
-                        pw = torch.empty_like(qw)
-                        Q.qlin_pack_weights(scheme, qw, pw)
-                        keep.append(pw)
-                        psegs.append((pw, sw, y))
-                    packed.linear_packed(scheme, x, psegs, qx=q, sx=s)
-                    packed.outputs = getattr(packed, "outputs", []) + [y for _, _, y in segs]
-    return full, prod, fused, swiglu, packed, ops, keep
+                packed.linear_packed(scheme, x, psegs, qx=q, sx=s)
+                packed.outputs += [y for _, _, y in segs]
+    return full, prod, fused, swiglu, packed, packed_all, ops, keep
 
 
 def layer_set(torch, Q, W, scheme, shapes, M, layers, dev, seed0):
@@ -538,16 +539,16 @@ def main():
         copy_calibration()
         for variant in args.prefill_variants.split(","):
             for M in (int(m) for m in args.prefill_m.split(",")):
-                _, _, fused, _, packed, ops, keep = prefill_layer_set(
+                _, _, fused, _, packed, packed_all, ops, keep = prefill_layer_set(
                     torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
-                run = packed if args.prefill_packed and packed is not None else fused
+                run = packed if args.prefill_packed else fused
                 torch.cuda.synchronize()
                 for _ in range(3):
                     run.run()
                 torch.cuda.synchronize()
                 log(f"prefill workload {variant}{' packed' if run is packed else ''}: M={M}, 4 layers, "
                     f"{len(run.calls)} calls per pass x3, {ops} ops per pass")
-                del keep, fused, packed, run
+                del keep, fused, packed, packed_all, run
         return
     if args.smallm_workload:
         copy_calibration()
@@ -760,18 +761,20 @@ def main():
         for variant, peak in (("int8", MFMA_INT8_PEAK_TOPS), ("fp8_row", MFMA_FP8_PEAK_TOPS),
                               ("fp8_block", MFMA_FP8_PEAK_TOPS)):
             for M in (512, 1024):
-                full, prod, fused, swiglu, packed, ops, keep = prefill_layer_set(
+                full, prod, fused, swiglu, packed, packed_all, ops, keep = prefill_layer_set(
                     torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
                 f_full = capture(torch, full.run, use_graph)
                 f_prod = capture(torch, prod.run, use_graph)
                 f_fused = capture(torch, fused.run, use_graph)
                 f_sg = capture(torch, swiglu.run, use_graph)
-                f_pk = capture(torch, packed.run, use_graph) if packed is not None else None
+                f_pk = capture(torch, packed.run, use_graph)
+                f_pa = capture(torch, packed_all.run, use_graph)
                 t_full = time_warm(torch, f_full)
                 t_prod = time_warm(torch, f_prod)
                 t_fused = time_warm(torch, f_fused)
                 t_sg = time_warm(torch, f_sg)
-                t_pk = time_warm(torch, f_pk) if f_pk is not None else None
+                t_pk = time_warm(torch, f_pk)
+                t_pa = time_warm(torch, f_pa)
                 key = f"prefill_{variant}_M{M}"
                 secondary[key] = {
                     "tops_fused_linear": round(ops / (t_fused * 1e-3) / 1e12, 1),
@@ -783,28 +786,28 @@ def main():
                     "tops_fused_linear_swiglu": round(ops / (t_sg * 1e-3) / 1e12, 1),
                     "shapes": "qwen3-8b" if variant == "fp8_block" else "llama-3.1-8b",
                 }
-                if t_pk is not None:
-                    # same outputs as the row-major calls (int8: bit for bit)
-                    swiglu.run()
-                    torch.cuda.synchronize()
-                    ref = [y.clone() for y in packed.outputs]
-                    for y in packed.outputs:
-                        y.fill_(0)
-                    packed.run()
-                    torch.cuda.synchronize()
-                    if variant == "int8":
-                        same = all(torch.equal(a, b) for a, b in zip(ref, packed.outputs))
-                    else:
-                        same = all(((a.view(torch.bfloat16).float() - b.view(torch.bfloat16).float()).abs().max()
-                                    <= 4e-3 * a.view(torch.bfloat16).float().abs().max()).item()
-                                   for a, b in zip(ref, packed.outputs))
-                    secondary[key]["packed_matches_row_major"] = bool(same)
-                    del ref
-                    secondary[key]["tops_packed_qkv_o_down_swiglu"] = round(ops / (t_pk * 1e-3) / 1e12, 1)
-                    secondary[key]["frac_packed_qkv_o_down_swiglu"] = round(ops / (t_pk * 1e-3) / 1e12 / peak, 4)
-                    secondary[key]["ms_per_layer_packed"] = round(t_pk / 4, 4)
+                # same outputs as the row-major calls (int8: bit for bit)
+                swiglu.run()
+                torch.cuda.synchronize()
+                ref = [y.clone() for y in packed.outputs]
+                for y in packed.outputs:
+                    y.fill_(0)
+                packed.run()
+                torch.cuda.synchronize()
+                if variant == "int8":
+                    same = all(torch.equal(a, b) for a, b in zip(ref, packed.outputs))
+                else:
+                    same = all(((a.view(torch.bfloat16).float() - b.view(torch.bfloat16).float()).abs().max()
+                                <= 4e-3 * a.view(torch.bfloat16).float().abs().max()).item()
+                               for a, b in zip(ref, packed.outputs))
+                secondary[key]["packed_matches_row_major"] = bool(same)
+                del ref
+                secondary[key]["tops_packed_qkv_o_down_swiglu"] = round(ops / (t_pk * 1e-3) / 1e12, 1)
+                secondary[key]["frac_packed_qkv_o_down_swiglu"] = round(ops / (t_pk * 1e-3) / 1e12 / peak, 4)
+                secondary[key]["ms_per_layer_packed"] = round(t_pk / 4, 4)
+                secondary[key]["tops_packed_all"] = round(ops / (t_pa * 1e-3) / 1e12, 1)
                 log(f"{key}: {secondary[key]}")
-                del keep, full, prod, fused, swiglu, packed, f_full, f_prod, f_fused, f_sg, f_pk
+                del keep, full, prod, fused, swiglu, packed, packed_all, f_full, f_prod, f_fused, f_sg, f_pk, f_pa
                 torch.cuda.synchronize()
 
     cpu = None

@@ -297,22 +297,24 @@ qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M,
  *
  * qlin_pack_weights: q_w row-major [N, K] codes in, q_w_packed [N * K bytes]
  * out (caller-owned device memory, 16-byte aligned, not overlapping q_w).
- * scheme QLIN_SCHEME_W8A8 or QLIN_SCHEME_FP8_ROWWISE (FP8_BLOCK:
- * QLIN_ERR_UNSUPPORTED); N % 128 == 0 and K % 128 == 0 (else QLIN_ERR_SHAPE);
- * N == 0 is a no-op.  One launch on stream; the scales are not touched (s_w
- * stays per row, in row order). */
+ * Any scheme (the block scheme's E4M3 codes take the FP8_ROWWISE layout);
+ * N % 128 == 0 and K % 128 == 0 (else QLIN_ERR_SHAPE); N == 0 is a no-op.
+ * One launch on stream; the scales are not touched (s_w keeps its layout:
+ * per row, or [N/128][K/128] blocks). */
 qlin_status qlin_pack_weights(qlin_scheme scheme, const void* q_w, int64_t N, int64_t K, void* q_w_packed,
                               hipStream_t stream);
 
 /* qlin_linear on packed weights: every segments[i].q_w is the qlin_pack_weights
  * output of that segment's codes (s_w and y as for qlin_linear).  Same results
  * as qlin_linear bit for bit for W8A8 (same int32 sums, same epilogue order);
- * FP8_ROWWISE within the tolerance of the FP8 paths (f32 sums, another
- * summation order).  For long inputs only: M >= 33 (smaller M:
- * QLIN_ERR_UNSUPPORTED, the one-row and small-M kernels read row-major
- * weights), every segment's n % 128 == 0 and K % 128 == 0 (QLIN_ERR_SHAPE),
- * scheme W8A8 or FP8_ROWWISE (FP8_BLOCK: QLIN_ERR_UNSUPPORTED); q_x / s_x are
- * required staging buffers as in the staged qlin_linear: one quantizer launch,
+ * the FP8 schemes within the tolerance of the FP8 paths (f32 sums, another
+ * summation order; the block scheme scales each 128-input block's partial sum
+ * by s_x[m][kb] * s_w[n/128][kb] into the f32 accumulator, as qlin_linear
+ * does, Qwen3 8B FP8 model card, "Loading").  For long inputs only: M >= 33
+ * (smaller M: QLIN_ERR_UNSUPPORTED, the one-row and small-M kernels read
+ * row-major weights), every segment's n % 128 == 0 and K % 128 == 0
+ * (QLIN_ERR_SHAPE); q_x / s_x are required staging buffers as in the staged
+ * qlin_linear (s_x [M][K/128] for the block scheme): one quantizer launch,
  * then one tiled launch over every segment (128 weight rows x 64 or 128 tokens
  * per tile).  Validation, aliasing rules and error behaviour as qlin_linear.
  * Packing pays on projections whose outputs give each CU at most a 128 x 128

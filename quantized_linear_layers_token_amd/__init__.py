@@ -261,7 +261,7 @@ def qlin_linear(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=No
 def qlin_pack_weights(scheme, q_w, q_w_packed, stream=None):
     """Reorders q_w [N, K] (1-byte codes, row-major) into the matrix-core
     operand order of qlin_linear_packed, written to q_w_packed (N * K bytes,
-    e.g. a tensor like q_w).  W8A8 and FP8 rowwise; N and K multiples of 128."""
+    e.g. a tensor like q_w).  Any scheme; N and K multiples of 128."""
     N, K = _dims2(q_w, "q_w", 1)
     _args(("q_w_packed", q_w_packed, N * K, 1), ("q_w", q_w, 0, None))
     _check(_lib.qlin_pack_weights(scheme, _ptr(q_w), N, K, _ptr(q_w_packed), _stream(stream)), "qlin_pack_weights")
@@ -270,10 +270,10 @@ def qlin_pack_weights(scheme, q_w, q_w_packed, stream=None):
 def qlin_linear_packed(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, stream=None):
     """qlin_linear for M >= 33 with every segment's q_w [n, K] in the packed
     order that qlin_pack_weights writes (s_w and y as for qlin_linear);
-    q_x / s_x staging required."""
+    q_x / s_x staging required (s_x [M, K/128] for the block scheme)."""
     M, K = _dims2(x, "x", 2)
     _args(*_segment_args(scheme, M, K, segments, out), ("q_x", q_x, M * K, 1),
-          ("s_x", s_x, 4 * _sx_count(False, M, K), 4), ("x", x, 0, None))
+          ("s_x", s_x, 4 * _sx_count(scheme == SCHEME_FP8_BLOCK, M, K), 4), ("x", x, 0, None))
     arr = segments_array(segments)
     _check(_lib.qlin_linear_packed(scheme, _ptr(x), M, K, arr, len(segments), out, _ptr(q_x), _ptr(s_x),
                                    _stream(stream)), "qlin_linear_packed")

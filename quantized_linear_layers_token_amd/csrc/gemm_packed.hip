@@ -50,15 +50,19 @@ __device__ __forceinline__ void pdma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, i
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
 }
 
-template <int V> struct PackedAcc { typedef v16i T; };
-template <> struct PackedAcc<VAR_FP8_ROW> { typedef v16f T; };
+template <int V> struct PackedAcc { typedef v16f T; };
+template <> struct PackedAcc<VAR_INT8> { typedef v16i T; };
+
+__device__ __forceinline__ void pdma4(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, voff, 0, 0, 0);
+}
 
 template <int V, int BM, int KG>
 __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode,
     int tiles_m, int tiles_n) {
     typedef typename PackedAcc<V>::T Acc;
-    static_assert(V == VAR_INT8 || V == VAR_FP8_ROW, "rowwise schemes");
+    constexpr bool BLK = V == VAR_FP8_BLOCK;
     constexpr int TM = BM / 32;                  // 32 x 32 MFMA tiles per wavefront (one weight row block)
     constexpr int BST = BM * 128;                // token bytes of one group stage
     constexpr int BW = BM / 32;                  // 1 KB token copies per wavefront and stage
@@ -68,9 +72,15 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     static_assert(2 * TM * 16 * 64 * 4 <= KG * BST || KG == 1, "two wavefronts' partial sums fit one ring array");
     // four distinct arrays: the compiler then knows which buffer a copy writes
     __shared__ __attribute__((aligned(1024))) uint8_t L0[KG * BST], L1[KG * BST], L2[KG * BST], L3[KG * BST];
-    // the epilogue's scales, copied straight into LDS (raw bf16 row scales, f32 token scales)
-    __shared__ __attribute__((aligned(16))) uint16_t s_w_raw[kPBN];
-    __shared__ __attribute__((aligned(16))) float s_x_t[BM];
+    // the epilogue's scales, copied straight into LDS (raw bf16 row scales, f32
+    // token scales); not used by block FP8
+    __shared__ __attribute__((aligned(16))) uint16_t s_w_raw[BLK ? 2 : kPBN];
+    __shared__ __attribute__((aligned(16))) float s_x_t[BLK ? 1 : BM];
+    // block FP8: each stage's token scales s_x[m][s] ride a ring of four more
+    // distinct arrays beside the token copies; wavefronts with no tokens to
+    // copy write zeros to a spare slot so every wavefront issues the same count
+    constexpr int XN = BLK ? KG * BM : 1;
+    __shared__ __attribute__((aligned(16))) float X0[XN], X1[XN], X2[XN], X3[XN], XS[BLK ? 64 : 1];
 
     const int tid = threadIdx.x;
     const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / kPGT);
@@ -106,6 +116,9 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     const __amdgpu_buffer_rsrc_t da = uniform_rsrc(wp + (int64_t)rb * 32 * K, 32 * K);
     const __amdgpu_buffer_rsrc_t db = uniform_rsrc(qx + (int64_t)m0 * K, min(BM, M - m0) * K);
     const int nk = K >> 7;
+    // block FP8: the tokens' scales s_x[m][*] and the tile's block scales s_w[n0 / 128][*]
+    const __amdgpu_buffer_rsrc_t dsx = uniform_rsrc(sx + (BLK ? (int64_t)m0 * nk : 0), BLK ? min(BM, M - m0) * nk * 4 : 0);
+    const __amdgpu_buffer_rsrc_t dsw = uniform_rsrc(sw + (BLK ? (int64_t)(n0 >> 7) * nk : 0), BLK ? nk * 2 : 0);
     const int nko = (nk + KG - 1) / KG;
     const int nsteps = (nko + 3) & ~3;           // whole unrolled iterations; steps past the end multiply zeros
     auto gs = [&](int i) { return KG * i + grp; };
@@ -114,7 +127,12 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
         constexpr int v = decltype(bi)::value;
         return (v == 0 ? L0 : v == 1 ? L1 : v == 2 ? L2 : L3) + grp * BST;
     };
+    auto xbuf = [&](auto bi) -> float* {
+        constexpr int v = decltype(bi)::value;
+        return (v == 0 ? X0 : v == 1 ? X1 : v == 2 ? X2 : X3) + grp * BM;
+    };
     v4u a0[4], a1[4], a2[4], a3[4];
+    uint32_t wsc[4];                             // block FP8: each stage's s_w, beside its weights
     auto aset = [&](auto bi) -> v4u(&)[4] {
         constexpr int v = decltype(bi)::value;
         if constexpr (v == 0) return a0;
@@ -138,6 +156,14 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
             const int r = blk * 8 + (lane >> 3);
             const int k = s * 128 + (((lane & 7) ^ pswz(r)) << 4);
             pdma16(db, dst + blk * 1024, k < K ? r * K + k : kPOOB);
+        }
+        if constexpr (BLK) {
+            // the stage's weight block scale (2 bytes, every lane) into register set bi
+            wsc[decltype(bi)::value] = __builtin_amdgcn_raw_buffer_load_b16(dsw, in ? 2 * s : kPOOB, 0, 0);
+            // wavefront w < BM / 64 copies the scales of tokens 64 w .. 64 w + 63
+            const bool real = wave < BM / 64;
+            const int tok = 64 * wave + lane;
+            pdma4(dsx, real ? (void*)(xbuf(bi) + 64 * wave) : (void*)XS, real && in ? (tok * nk + s) * 4 : kPOOB);
         }
     };
 
@@ -192,6 +218,51 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
         }
     };
 
+    // Block FP8, tile-major: token tile i's two MFMAs (the stage's two K
+    // slices, one 128-input block) start from zero, and the partial is scaled
+    // by s_x[m][s] * s_w[n0 / 128][s] into the accumulator while the next
+    // tile's MFMAs run (two partials live); tile i + 1's fragments are read
+    // while tile i is multiplied.
+    v8i bt[2][2];
+    v16f pt[2];
+    auto rdtile = [&](auto bi, int p, int i) {
+        const uint8_t* base = buf(bi);
+        auto rdq = [&](int r, int c) { return *reinterpret_cast<const v4i*>(base + r * 128 + ((c ^ pswz(r)) << 4)); };
+        const int r = i * 32 + (lane & 31);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const v4i lo = rdq(r, 4 * sub + 2 * half), hi = rdq(r, 4 * sub + 2 * half + 1);
+            bt[p][sub] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
+    };
+    auto compute_blk = [&](auto bi) {
+        const v4u(&ar)[4] = aset(bi);
+        const v8i a0v = v8i{(int)ar[0].x, (int)ar[0].y, (int)ar[0].z, (int)ar[0].w,
+                            (int)ar[1].x, (int)ar[1].y, (int)ar[1].z, (int)ar[1].w};
+        const v8i a1v = v8i{(int)ar[2].x, (int)ar[2].y, (int)ar[2].z, (int)ar[2].w,
+                            (int)ar[3].x, (int)ar[3].y, (int)ar[3].z, (int)ar[3].w};
+        // (stages past the end carry zero codes and zero scales)
+        const float fw = bf16_lo(wsc[decltype(bi)::value]);
+        float fx[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fx[i] = xbuf(bi)[i * 32 + (lane & 31)] * fw;
+#pragma unroll
+        for (int t = 0; t <= TM; ++t) {
+            if (t + 1 < TM) rdtile(bi, (t + 1) & 1, t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t < TM) {
+                pt[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0v, bt[t & 1][0], v16f{}, 0, 0, 0, 0, 0, 0);
+                pt[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1v, bt[t & 1][1], pt[t & 1], 0, 0, 0, 0, 0, 0);
+            }
+            if (t > 0) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[t - 1][e] = __builtin_fmaf(pt[(t - 1) & 1][e], fx[t - 1], acc[t - 1][e]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     // Step kt multiplies stage gs(kt) from register set / buffer kt % 4 once
     // this wavefront's loads of it are complete (the loads of the two later
     // stages may stay in flight: vmcnt <= 2 (4 + BW)) and every wavefront has
@@ -199,16 +270,16 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     // reads buffer (kt + 3) % 4), then issues stage gs(kt + 3) into set and
     // buffer (kt + 3) % 4.  The explicit s_barrier (no fence) leaves those
     // later copies in flight; the memory clobber keeps LDS reads after it.
-    constexpr int VMC = 2 * (4 + BW);
+    constexpr int VMC = 2 * (4 + BW + (BLK ? 2 : 0));
     constexpr int WIMM = (VMC & 15) | ((VMC >> 4) << 14) | 0x0F70;   // vmcnt(VMC), expcnt and lgkmcnt not waited
     // scales first (older than every stage load, so the first step's wait
     // covers them; no register waits for them): wavefront 0 of group 0 copies
     // the 128 row scales (256 bytes), wavefront 1 the BM token scales (tokens
     // past M read as zero and are never stored)
-    if (grp == 0 && wave == 0) {
+    if (!BLK && grp == 0 && wave == 0) {
         const __amdgpu_buffer_rsrc_t ds = uniform_rsrc(sw + n0, kPBN * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ds, (__attribute__((address_space(3))) void*)s_w_raw, 4, 4 * lane, 0, 0, 0);
-    } else if (grp == 0 && wave == 1) {
+    } else if (!BLK && grp == 0 && wave == 1) {
         const __amdgpu_buffer_rsrc_t ds = uniform_rsrc(sx + m0, min(BM, M - m0) * 4);
 #pragma unroll
         for (int j = 0; j < BM / 64; ++j)
@@ -230,11 +301,13 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
         __builtin_amdgcn_s_waitcnt(WIMM);
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        rdsub(bi, 0, 0);                         // in flight while the next stage's loads issue
+        if constexpr (BLK) rdtile(bi, 0, 0);    // in flight while the next stage's loads issue
+        else rdsub(bi, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         issue(PIC<(v + 3) & 3>{}, gs(kt + 3));
         __builtin_amdgcn_sched_barrier(0);
-        compute(bi);
+        if constexpr (BLK) compute_blk(bi);
+        else compute(bi);
     };
     // one loop exit (with an exit after every step the compiler drains every
     // load in flight at the top of the loop)
@@ -290,7 +363,7 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int ml = i * 32 + (lane & 31);
-                const float sxm = s_x_t[ml];
+                const float sxm = BLK ? 0.f : s_x_t[BLK ? 0 : ml];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int nl = wave * 32 + 8 * g + 4 * half;
@@ -298,6 +371,7 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         if constexpr (V == VAR_INT8) v[k] = (float)acc[i][4 * g + k] * (sxm * bf16_lo(s_w_raw[nl + k]));
+                        else if constexpr (BLK) v[k] = acc[i][4 * g + k];     // scaled per block in the loop
                         else v[k] = acc[i][4 * g + k] * (sxm * bf16_lo(s_w_raw[nl + k]));
                     }
                     const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
@@ -323,7 +397,7 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
         const int ml = i * 32 + (lane & 31);
         const int m = m0 + ml;
         if (m >= M) continue;
-        const float sxm = s_x_t[ml];
+        const float sxm = BLK ? 0.f : s_x_t[BLK ? 0 : ml];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int nl = wave * 32 + 8 * g + 4 * half;
@@ -332,6 +406,9 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
                 const int a[4] = {acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]};
                 const float w4[4] = {bf16_lo(s_w_raw[nl]), bf16_lo(s_w_raw[nl + 1]), bf16_lo(s_w_raw[nl + 2]), bf16_lo(s_w_raw[nl + 3])};
                 store4_rowwise_i32acc(y, idx, a, sxm, w4, mode);
+            } else if constexpr (BLK) {
+                const float v4[4] = {acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]};
+                store4_f32(y, idx, v4, mode);
             } else {
                 const float v4[4] = {acc[i][4 * g] * (sxm * bf16_lo(s_w_raw[nl])), acc[i][4 * g + 1] * (sxm * bf16_lo(s_w_raw[nl + 1])),
                                      acc[i][4 * g + 2] * (sxm * bf16_lo(s_w_raw[nl + 2])), acc[i][4 * g + 3] * (sxm * bf16_lo(s_w_raw[nl + 3]))};
@@ -363,12 +440,21 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
 template <int V, int BM, int KG>
 hipError_t launch_packed_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K,
                               int mode, hipStream_t st) {
-    const int tm = (int)((M + BM - 1) / BM);
-    int tn = 0;
+    const int64_t tm = (M + BM - 1) / BM;
+    int64_t tn = 0;
     for (int i = 0; i < sa.nseg; ++i) tn += (sa.start[i + 1] - sa.start[i]) / kPBN;
+    if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_packed_kernel<V, BM, KG>), dim3((unsigned)(tm * tn)), dim3(kPGT * KG), 0, st, qx, sx, sa,
-                       (int)M, (int)K, mode, tm, tn);
+                       (int)M, (int)K, mode, (int)tm, (int)tn);
     return hipGetLastError();
+}
+
+template <int V>
+hipError_t launch_packed_shape(int shape, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
+                               int64_t K, int mode, hipStream_t st) {
+    return shape == 2   ? launch_packed_tile<V, 128, 1>(qx, sx, sa, M, K, mode, st)
+           : shape == 1 ? launch_packed_tile<V, 128, 2>(qx, sx, sa, M, K, mode, st)
+                        : launch_packed_tile<V, 64, 2>(qx, sx, sa, M, K, mode, st);
 }
 
 }  // namespace
@@ -385,14 +471,9 @@ hipError_t launch_gemm_packed(int variant, const uint8_t* qx, const float* sx, c
     for (int i = 0; i < sa.nseg; ++i) panels += (sa.start[i + 1] - sa.start[i]) / kPBN;
     const int64_t t128 = ((M + 127) / 128) * panels;
     const int shape = t128 > 256 ? 2 : t128 >= 192 ? 1 : 0;
-    if (variant == VAR_INT8)
-        return shape == 2   ? launch_packed_tile<VAR_INT8, 128, 1>(qx, sx, sa, M, K, mode, st)
-               : shape == 1 ? launch_packed_tile<VAR_INT8, 128, 2>(qx, sx, sa, M, K, mode, st)
-                            : launch_packed_tile<VAR_INT8, 64, 2>(qx, sx, sa, M, K, mode, st);
-    if (variant == VAR_FP8_ROW)
-        return shape == 2   ? launch_packed_tile<VAR_FP8_ROW, 128, 1>(qx, sx, sa, M, K, mode, st)
-               : shape == 1 ? launch_packed_tile<VAR_FP8_ROW, 128, 2>(qx, sx, sa, M, K, mode, st)
-                            : launch_packed_tile<VAR_FP8_ROW, 64, 2>(qx, sx, sa, M, K, mode, st);
+    if (variant == VAR_INT8) return launch_packed_shape<VAR_INT8>(shape, qx, sx, sa, M, K, mode, st);
+    if (variant == VAR_FP8_ROW) return launch_packed_shape<VAR_FP8_ROW>(shape, qx, sx, sa, M, K, mode, st);
+    if (variant == VAR_FP8_BLOCK) return launch_packed_shape<VAR_FP8_BLOCK>(shape, qx, sx, sa, M, K, mode, st);
     return hipErrorInvalidValue;
 }
 
@@ -401,7 +482,7 @@ hipError_t launch_pack_weights(int variant, const uint8_t* w, int64_t N, int64_t
     const int64_t blocks = (units + 255) / 256;
     const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
     if (variant == VAR_INT8) hipLaunchKernelGGL((pack_weights_kernel<32>), dim3(grid), dim3(256), 0, st, w, p, units, (int)K);
-    else if (variant == VAR_FP8_ROW)
+    else if (variant == VAR_FP8_ROW || variant == VAR_FP8_BLOCK)
         hipLaunchKernelGGL((pack_weights_kernel<64>), dim3(grid), dim3(256), 0, st, w, p, units, (int)K);
     else return hipErrorInvalidValue;
     return hipGetLastError();

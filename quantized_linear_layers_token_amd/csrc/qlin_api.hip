@@ -236,12 +236,14 @@ qlin_status qlin_linear(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_
 
 qlin_status qlin_pack_weights(qlin_scheme scheme, const void* q_w, int64_t N, int64_t K, void* q_w_packed,
                               hipStream_t stream) {
-    if (scheme != QLIN_SCHEME_W8A8 && scheme != QLIN_SCHEME_FP8_ROWWISE) return QLIN_ERR_UNSUPPORTED;
+    if (scheme != QLIN_SCHEME_W8A8 && scheme != QLIN_SCHEME_FP8_ROWWISE && scheme != QLIN_SCHEME_FP8_BLOCK)
+        return QLIN_ERR_UNSUPPORTED;
     if (!valid_mn(N) || !valid_k(K) || (N % 128) != 0 || (K % 128) != 0) return QLIN_ERR_SHAPE;
     if (N == 0) return QLIN_OK;
     if (!q_w || !q_w_packed) return QLIN_ERR_NULL;
     if (!aligned(q_w, 16) || !aligned(q_w_packed, 16)) return QLIN_ERR_ALIGN;
     if (overlap(rng(q_w, N * K), rng(q_w_packed, N * K))) return QLIN_ERR_ALIAS;
+    // the block scheme's codes are E4M3 like the rowwise one's: same layout
     const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8 : qlin::VAR_FP8_ROW;
     return hip_status(qlin::launch_pack_weights(variant, static_cast<const uint8_t*>(q_w), N, K,
                                                 static_cast<uint8_t*>(q_w_packed), stream));
@@ -250,7 +252,6 @@ qlin_status qlin_pack_weights(qlin_scheme scheme, const void* q_w, int64_t N, in
 qlin_status qlin_linear_packed(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
                                const qlin_segment* segments, int32_t nseg, qlin_out out, void* q_x, float* s_x,
                                hipStream_t stream) {
-    if (scheme != QLIN_SCHEME_W8A8 && scheme != QLIN_SCHEME_FP8_ROWWISE) return QLIN_ERR_UNSUPPORTED;
     bool noop = false;
     // the staged form's checks (staging buffers required)
     const qlin_status st = check_linear(scheme, x, M, K, segments, nseg, out, q_x, s_x, false, &noop);
@@ -259,7 +260,8 @@ qlin_status qlin_linear_packed(qlin_scheme scheme, const uint16_t* x, int64_t M,
     for (int i = 0; i < nseg; ++i)
         if ((segments[i].n % 128) != 0) return QLIN_ERR_SHAPE;
     if (M < 33) return QLIN_ERR_UNSUPPORTED;
-    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8 : qlin::VAR_FP8_ROW;
+    const int variant = scheme == QLIN_SCHEME_W8A8 ? qlin::VAR_INT8
+                        : scheme == QLIN_SCHEME_FP8_ROWWISE ? qlin::VAR_FP8_ROW : qlin::VAR_FP8_BLOCK;
     qlin::SegmentArgs sa{};
     int n = 0, k = 0;
     for (int i = 0; i < nseg; ++i) {
@@ -275,7 +277,8 @@ qlin_status qlin_linear_packed(qlin_scheme scheme, const uint16_t* x, int64_t M,
     for (int i = k; i <= qlin::kMaxSegments; ++i) sa.start[i] = n;
     hipError_t e;
     if (variant == qlin::VAR_INT8) e = qlin::launch_quant_int8(x, M, K, static_cast<int8_t*>(q_x), s_x, stream);
-    else e = qlin::launch_quant_fp8(x, M, K, 0, static_cast<uint8_t*>(q_x), s_x, stream);
+    else e = qlin::launch_quant_fp8(x, M, K, variant == qlin::VAR_FP8_BLOCK ? 128 : 0, static_cast<uint8_t*>(q_x),
+                                    s_x, stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(qlin::launch_gemm_packed(variant, static_cast<const uint8_t*>(q_x), s_x, sa, M, K, (int)out,
                                                stream));

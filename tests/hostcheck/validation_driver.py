@@ -119,7 +119,8 @@ wide = segs((A + 0x1000000, A + 0x2000000, A + 0x3000000, 128), (A + 0x4000000, 
 assert call("qlin_linear_packed", 0, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == OK
 assert call("qlin_linear_packed", 0, x, 32, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == UNSUP
 assert call("qlin_linear_packed", 0, x, 64, 256, three, 3, 0, A + 0xA000000, A + 0xB000000, None) == SHAPE
-assert call("qlin_linear_packed", 2, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == UNSUP
+assert call("qlin_linear_packed", 2, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == OK
+assert call("qlin_linear_packed", 9, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == UNSUP
 assert call("qlin_pack_weights", 1, A, 256, 384, A + 0x1000000, None) == OK
 assert call("qlin_pack_weights", 1, A, 256, 384, A + 0x100, None) == ALIAS
 assert call("qlin_pack_weights", 0, A, 200, 384, A + 0x1000000, None) == SHAPE

@@ -217,7 +217,6 @@ def test_linear_swiglu_validation():
 def test_pack_weights_validation():
     pk = L.qlin_pack_weights
     w, p = A, A + 0x1000000
-    assert pk(2, w, 256, 384, p, None) == Q.QLIN_ERR_UNSUPPORTED      # block scheme: not packed
     assert pk(9, w, 256, 384, p, None) == Q.QLIN_ERR_UNSUPPORTED
     assert pk(0, w, 200, 384, p, None) == Q.QLIN_ERR_SHAPE            # N % 128
     assert pk(1, w, 256, 400, p, None) == Q.QLIN_ERR_SHAPE            # K % 128
@@ -236,7 +235,8 @@ def test_linear_packed_validation():
                      Seg(A + 0x4000000, A + 0x5000000, A + 0x6000000, 256))
     odd = (Seg * 1)(Seg(A + 0x1000000, A + 0x2000000, A + 0x3000000, 64))
     lp = L.qlin_linear_packed
-    assert lp(2, x, 64, 256, segs, 2, 0, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED   # block scheme
+    assert lp(9, x, 64, 256, segs, 2, 0, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED   # unknown scheme
+    assert lp(2, x, 64, 256, segs, 2, Q.OUT_I32, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED
     assert lp(0, x, 32, 256, segs, 2, 0, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED   # M <= 32: row-major kernels
     assert lp(0, x, 64, 256, odd, 1, 0, qx, sx, None) == Q.QLIN_ERR_SHAPE          # n % 128
     assert lp(0, x, 64, 272, segs, 2, 0, qx, sx, None) == Q.QLIN_ERR_SHAPE         # K % 128

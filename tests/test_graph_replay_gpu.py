@@ -2,7 +2,7 @@
 form of qlin_linear / qlin_linear_swiglu (one token; two tokens; four tokens
 rounded in the small-M kernel; quantizer + small-M kernel; quantizer + tiled
 GEMM, including its 8-wavefront 256 x 256 tile; quantizer + the packed-weight
-GEMM on both token-tile widths) must reproduce the eager results bit for bit on every replay, with
+GEMM on both token-tile widths, block FP8 included) must reproduce the eager results bit for bit on every replay, with
 eager work (output poisoning, another library call) between the replays."""
 import numpy as np
 import pytest
@@ -50,7 +50,8 @@ def build(torch):
     outs += [qx, sx]
     calls.append(lambda x=x, segs=segs, qx=qx, sx=sx: Q().qlin_linear(FP8R, x, segs, q_x=qx, s_x=sx))
     # packed weights: W8A8 on 64-token tiles, FP8 rowwise on 128-token tiles
-    for i, (scheme, M, K, ns) in enumerate([(W8A8, 100, 512, [256, 128]), (FP8R, 300, 256, [4096, 4096])]):
+    for i, (scheme, M, K, ns) in enumerate([(W8A8, 100, 512, [256, 128]), (FP8R, 300, 256, [4096, 4096]),
+                                            (FP8B, 150, 512, [256, 128])]):
         x = dev(W.x_bf16(9960 + i, M, K))
         segs = []
         for j, n in enumerate(ns):
@@ -58,10 +59,11 @@ def build(torch):
             pw = torch.empty_like(qw)
             Q().qlin_pack_weights(scheme, qw, pw)
             y = empty(torch, (M, n), torch.int16)
-            segs.append((pw, dev(W.scale_bf16(9966 + 2 * i + j, (n,))), y))
+            sws = (n // 128, K // 128) if scheme == FP8B else (n,)
+            segs.append((pw, dev(W.scale_bf16(9966 + 2 * i + j, sws)), y))
             outs.append(y)
         qx = empty(torch, (M, K), torch.uint8)
-        sx = empty(torch, (M,), torch.float32)
+        sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32)
         outs += [qx, sx]
         calls.append(lambda s=scheme, x=x, segs=segs, qx=qx, sx=sx: Q().qlin_linear_packed(s, x, segs, q_x=qx, s_x=sx))
     for i, (M, K) in enumerate([(1, 4096), (4, 1024), (40, 512)]):

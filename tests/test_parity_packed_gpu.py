@@ -2,9 +2,10 @@
 definition (a numpy reshape/transpose of the row-major codes, written from the
 layout formula in include/qlin.h), and qlin_linear_packed against the CPU
 oracle -- W8A8 bit for bit (same int32 sums, same f32 epilogue order; the
-int32 accumulator output exactly), FP8 rowwise within the FP8 tolerance --
-on 64- and 128-token tiles, ragged token tails, several segments, and the
-q/k/v, o and down shapes of an 8B model at 512 tokens."""
+int32 accumulator output exactly), FP8 rowwise and block FP8 within the FP8
+tolerance -- on 64- and 128-token tiles, one and two K groups, ragged token
+tails, several segments, and the q/k/v, o and down shapes of an 8B model at
+512 tokens (Qwen3 8B's for the block scheme)."""
 import numpy as np
 import pytest
 
@@ -14,7 +15,7 @@ from gpu_helpers import assert_within_tol, dev, empty, host, torch_mod
 
 pytestmark = pytest.mark.gpu
 BF16, I32, F32 = 0, 1, 2
-W8A8, FP8R = 0, 1
+W8A8, FP8R, FP8B = 0, 1, 2
 
 
 def Q():
@@ -49,7 +50,7 @@ def test_packed_reference_is_a_permutation_with_the_stated_entries():
         assert np.array_equal(np.sort(p), np.sort(w.reshape(-1)))
 
 
-@pytest.mark.parametrize("scheme,S", [(W8A8, 32), (FP8R, 64)])
+@pytest.mark.parametrize("scheme,S", [(W8A8, 32), (FP8R, 64), (FP8B, 64)])
 @pytest.mark.parametrize("N,K", [(128, 128), (384, 1024), (256, 14336)])
 def test_pack_weights_layout(scheme, S, N, K):
     torch = torch_mod()
@@ -67,7 +68,7 @@ def packed_segments(scheme, seed, ns, K):
     out = []
     for i, n in enumerate(ns):
         qw = W.w_int8(seed + 10 * i, n, K) if scheme == W8A8 else W.w_e4m3(seed + 10 * i, n, K)
-        sw = W.scale_bf16(seed + 10 * i + 1, (n,))
+        sw = W.scale_bf16(seed + 10 * i + 1, (n // 128, K // 128) if scheme == FP8B else (n,))
         pw = empty(torch, (n, K), torch.uint8)
         Q().qlin_pack_weights(scheme, dev(qw), pw)
         out.append((qw, sw, pw))
@@ -80,7 +81,7 @@ def run_packed(scheme, x, segs, out):
     esz = 2 if out == BF16 else 4
     ys = [empty(torch, (M * qw.shape[0] * esz + 64,), torch.uint8, fill=0xFF) for qw, _, _ in segs]
     qx = empty(torch, (M, K), torch.uint8, fill=0x55)
-    sx = empty(torch, (M,), torch.float32, fill=0x55)
+    sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32, fill=0x55)
     Q().qlin_linear_packed(scheme, dev(x), [(pw, dev(sw), y) for (_, sw, pw), y in zip(segs, ys)], out=out,
                            q_x=qx, s_x=sx)
     res = []
@@ -93,30 +94,45 @@ def run_packed(scheme, x, segs, out):
 
 
 CASES = [
-    # (M, K, segment widths): token tiles of 64 unless tiles x panels >= 192
+    # (M, K, segment widths): 128 x 64 tiles with two K groups below 192 tiles of
+    # 128 x 128, 128 x 128 with two K groups up to 256, with one K group past it
     (33, 128, [128]),                       # smallest M, one tile, 31 rows past M
     (64, 256, [128, 256]),                  # exactly one tile, two segments
     (200, 1024, [384, 128]),                # ragged last tile (8 tokens)
     (130, 512, [1024, 256, 256]),           # q/k/v-shaped segments, 2 tokens in the last tile
     (300, 256, [4096, 4096]),               # 128-token tiles (3 x 64 panels), ragged 44
     (97, 4096, [640, 128, 512, 256]),       # four segments, long K
+    (1100, 256, [2048, 2048]),              # past 256 tiles of 128 x 128 (9 x 32): one K group, ragged 76
+    (2000, 128, [2304]),                    # one K group (16 x 18 tiles), one K stage only
 ]
 
 
-@pytest.mark.parametrize("scheme", [W8A8, FP8R])
+def oracle_quant(scheme, x):
+    if scheme == W8A8:
+        return O.quant_act_int8(x)
+    return O.quant_act_fp8(x, 128 if scheme == FP8B else 0)
+
+
+def exact(scheme, qx, sx, qw, sw):
+    if scheme == W8A8:
+        return O.rescale_rowwise(O.contract_int8(qx, qw), sx, sw)
+    if scheme == FP8R:
+        return O.rescale_rowwise(O.contract_e4m3(qx, qw), sx, sw)
+    return O.rescale_block(O.contract_e4m3_blocks(qx, qw), sx, sw)
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R, FP8B])
 @pytest.mark.parametrize("M,K,ns", CASES)
 def test_linear_packed_matches_oracle(scheme, M, K, ns):
     x = W.x_bf16(8100 + M + K + len(ns), M, K)
     segs = packed_segments(scheme, 8200 + K, ns, K)
-    qx_ref, sx_ref = O.quant_act_int8(x) if scheme == W8A8 else O.quant_act_fp8(x, 0)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
     ys = run_packed(scheme, x, segs, BF16)
     for (qw, sw, _), y in zip(segs, ys):
         if scheme == W8A8:
             acc = O.contract_int8(qx_ref, qw)
             assert np.array_equal(y, O.epilogue_f32_order(acc, sx_ref, sw))
-            assert_within_tol(y, O.rescale_rowwise(acc, sx_ref, sw), "packed W8A8")
-        else:
-            assert_within_tol(y, O.rescale_rowwise(O.contract_e4m3(qx_ref, qw), sx_ref, sw), "packed FP8 rowwise")
+        assert_within_tol(y, exact(scheme, qx_ref, sx_ref, qw, sw), f"packed scheme {scheme}")
 
 
 @pytest.mark.parametrize("M", [100, 300])
@@ -133,30 +149,48 @@ def test_linear_packed_int8_accumulator_and_f32_exact(M):
         assert_within_tol(yf, O.rescale_rowwise(acc, sx_ref, sw), "packed W8A8 f32", f32=True)
 
 
-def test_linear_packed_fp8_f32_output():
+@pytest.mark.parametrize("scheme", [FP8R, FP8B])
+def test_linear_packed_fp8_f32_output(scheme):
     M, K = 150, 1024
     x = W.x_bf16(8400, M, K)
-    segs = packed_segments(FP8R, 8401, [256, 512], K)
-    qx_ref, sx_ref = O.quant_act_fp8(x, 0)
-    for (qw, sw, _), y in zip(segs, run_packed(FP8R, x, segs, F32)):
-        assert_within_tol(y, O.rescale_rowwise(O.contract_e4m3(qx_ref, qw), sx_ref, sw), "packed FP8 f32", f32=True)
+    segs = packed_segments(scheme, 8401, [256, 512], K)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
+    for (qw, sw, _), y in zip(segs, run_packed(scheme, x, segs, F32)):
+        assert_within_tol(y, exact(scheme, qx_ref, sx_ref, qw, sw), "packed FP8 f32", f32=True)
 
 
-@pytest.mark.parametrize("scheme", [W8A8, FP8R])
-@pytest.mark.parametrize("name,K,ns", [("qkv", 4096, [4096, 1024, 1024]), ("o", 4096, [4096]),
-                                       ("down", 14336, [4096])])
-def test_linear_packed_llama8b_512_tokens(scheme, name, K, ns):
+def test_linear_packed_block_long_k():
+    # 112 and 129 K blocks (an odd count: the last bf16 block scale ends two
+    # bytes before a 4-byte boundary of the scale row)
+    for K in (14336, 16512):
+        M = 40
+        x = W.x_bf16(8450 + K, M, K)
+        segs = packed_segments(FP8B, 8451, [256], K)
+        qx_ref, sx_ref = oracle_quant(FP8B, x)
+        (qw, sw, _), = segs
+        y, = run_packed(FP8B, x, segs, BF16)
+        assert_within_tol(y, exact(FP8B, qx_ref, sx_ref, qw, sw), f"packed block K={K}")
+
+
+LLAMA = [("qkv", 4096, [4096, 1024, 1024]), ("o", 4096, [4096]), ("down", 14336, [4096])]
+QWEN3 = [("qkv", 4096, [4096, 1024, 1024]), ("o", 4096, [4096]), ("down", 12288, [4096]),
+         ("gateup", 4096, [12288, 12288])]
+
+
+@pytest.mark.parametrize("scheme,name,K,ns", [(s, *c) for s in (W8A8, FP8R) for c in LLAMA] +
+                         [(FP8B, *c) for c in QWEN3])
+def test_linear_packed_8b_512_tokens(scheme, name, K, ns):
     # the projections the packed path serves, at the prefill size it is timed on
     M = 512
     x = W.x_bf16(8500 + K, M, K)
     segs = packed_segments(scheme, 8600 + K, ns, K)
-    qx_ref, sx_ref = O.quant_act_int8(x) if scheme == W8A8 else O.quant_act_fp8(x, 0)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
     ys = run_packed(scheme, x, segs, BF16)
     for (qw, sw, _), y in zip(segs, ys):
         if scheme == W8A8:
             assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw)), name
         else:
-            assert_within_tol(y, O.rescale_rowwise(O.contract_e4m3(qx_ref, qw), sx_ref, sw), name)
+            assert_within_tol(y, exact(scheme, qx_ref, sx_ref, qw, sw), name)
 
 
 def test_linear_packed_matches_row_major_path():
@@ -175,7 +209,7 @@ def test_linear_packed_matches_row_major_path():
     assert torch.equal(y1, y2)
 
 
-def test_linear_packed_refuses_small_m_and_block_scheme():
+def test_linear_packed_refuses_small_m():
     torch = torch_mod()
     K, n = 256, 128
     x = dev(W.x_bf16(8800, 32, K))
@@ -186,5 +220,5 @@ def test_linear_packed_refuses_small_m_and_block_scheme():
     with pytest.raises(Q().QlinError):
         Q().qlin_linear_packed(W8A8, x, [(pw, sw, y)], q_x=qx, s_x=sx)
     with pytest.raises(Q().QlinError):
-        Q().qlin_pack_weights(2, pw, torch.empty_like(pw))
+        Q().qlin_pack_weights(9, pw, torch.empty_like(pw))
     assert (host(y).view(np.uint8) == 0x3C).all()      # nothing launched
