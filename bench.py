@@ -71,7 +71,7 @@ def parse():
                     help="comma list of int8, fp8_row, fp8_block for --prefill-workload")
     ap.add_argument("--prefill-m", default="512", help="comma list of token counts for --prefill-workload")
     ap.add_argument("--prefill-packed", action="store_true",
-                    help="--prefill-workload runs q/k/v, o and down on packed weights (gate/up as SwiGLU)")
+                    help="--prefill-workload runs every projection on packed weights (gate/up as SwiGLU)")
     ap.add_argument("--smallm-workload", action="store_true",
                     help="for kernel traces and counters of the small-M path: a 1 GiB copy, then the W8A8 "
                          "projection M=16 N=K=4096 (32 weight copies) and the W8A8 Llama layer set at M=4, 16, "
@@ -133,6 +133,14 @@ class Launcher:
                                                         gate[0].shape[0], h.data_ptr(),
                                                         None if qx is None else qx.data_ptr(),
                                                         None if sx is None else sx.data_ptr())))
+
+    def linear_swiglu_packed(self, scheme, x, gate, up, h, qx, sx):
+        """gate, up: (packed q_w, s_w) of one MLP; h [M, I] receives silu(gate) * up."""
+        M, K = x.shape
+        self.calls.append((self.L.qlin_linear_swiglu_packed, (scheme, x.data_ptr(), M, K, gate[0].data_ptr(),
+                                                               gate[1].data_ptr(), up[0].data_ptr(), up[1].data_ptr(),
+                                                               gate[0].shape[0], h.data_ptr(), qx.data_ptr(),
+                                                               sx.data_ptr())))
 
     def gemm(self, fn, qx, sx, qw, sw, y, M, N, K, out=0, path=0):
         f = getattr(self.L, fn + "_ex")
@@ -298,6 +306,7 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
     fused = Launcher(Q, torch)
     swiglu = Launcher(Q, torch)     # fused, with gate/up as one SwiGLU launch
     packed = Launcher(Q, torch)     # swiglu's calls with q/k/v, o and down on packed weights
+    packed_sg = Launcher(Q, torch)  # swiglu's calls, every projection on packed weights
     packed_all = Launcher(Q, torch)  # fused's calls, every projection on packed weights
     packed.outputs = []
     scheme = {"int8": Q.SCHEME_W8A8, "fp8_row": Q.SCHEME_FP8_ROWWISE, "fp8_block": Q.SCHEME_FP8_BLOCK}[variant]
@@ -347,10 +356,13 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
             if group == ("gate", "up"):
                 swiglu.linear_swiglu(scheme, x, segs[0][:2], segs[1][:2], segs[0][2], qx=q, sx=s)
                 packed.linear_swiglu(scheme, x, segs[0][:2], segs[1][:2], segs[0][2], qx=q, sx=s)
+                packed_sg.linear_swiglu_packed(scheme, x, psegs[0][:2], psegs[1][:2], segs[0][2], q, s)
             else:
                 swiglu.linear(scheme, x, segs, qx=q, sx=s)
                 packed.linear_packed(scheme, x, psegs, qx=q, sx=s)
+                packed_sg.linear_packed(scheme, x, psegs, qx=q, sx=s)
                 packed.outputs += [y for _, _, y in segs]
+    packed.sg_launcher = packed_sg
     return full, prod, fused, swiglu, packed, packed_all, ops, keep
 
 
@@ -541,7 +553,7 @@ def main():
             for M in (int(m) for m in args.prefill_m.split(",")):
                 _, _, fused, _, packed, packed_all, ops, keep = prefill_layer_set(
                     torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
-                run = packed if args.prefill_packed else fused
+                run = packed.sg_launcher if args.prefill_packed else fused
                 torch.cuda.synchronize()
                 for _ in range(3):
                     run.run()
@@ -769,12 +781,14 @@ def main():
                 f_sg = capture(torch, swiglu.run, use_graph)
                 f_pk = capture(torch, packed.run, use_graph)
                 f_pa = capture(torch, packed_all.run, use_graph)
+                f_ps = capture(torch, packed.sg_launcher.run, use_graph)
                 t_full = time_warm(torch, f_full)
                 t_prod = time_warm(torch, f_prod)
                 t_fused = time_warm(torch, f_fused)
                 t_sg = time_warm(torch, f_sg)
                 t_pk = time_warm(torch, f_pk)
                 t_pa = time_warm(torch, f_pa)
+                t_ps = time_warm(torch, f_ps)
                 key = f"prefill_{variant}_M{M}"
                 secondary[key] = {
                     "tops_fused_linear": round(ops / (t_fused * 1e-3) / 1e12, 1),
@@ -806,8 +820,10 @@ def main():
                 secondary[key]["frac_packed_qkv_o_down_swiglu"] = round(ops / (t_pk * 1e-3) / 1e12 / peak, 4)
                 secondary[key]["ms_per_layer_packed"] = round(t_pk / 4, 4)
                 secondary[key]["tops_packed_all"] = round(ops / (t_pa * 1e-3) / 1e12, 1)
+                secondary[key]["tops_packed_all_swiglu"] = round(ops / (t_ps * 1e-3) / 1e12, 1)
+                secondary[key]["frac_packed_all_swiglu"] = round(ops / (t_ps * 1e-3) / 1e12 / peak, 4)
                 log(f"{key}: {secondary[key]}")
-                del keep, full, prod, fused, swiglu, packed, packed_all, f_full, f_prod, f_fused, f_sg, f_pk, f_pa
+                del keep, full, prod, fused, swiglu, packed, packed_all, f_full, f_prod, f_fused, f_sg, f_pk, f_pa, f_ps
                 torch.cuda.synchronize()
 
     cpu = None

@@ -324,6 +324,20 @@ qlin_status qlin_linear_packed(qlin_scheme scheme, const uint16_t* x, int64_t M,
                                const qlin_segment* segments, int32_t nseg, qlin_out out,
                                void* q_x, float* s_x, hipStream_t stream);
 
+/* qlin_linear_swiglu on packed weights: gate_q_w_packed and up_q_w_packed are
+ * the qlin_pack_weights outputs of the gate and up codes ([I, K] each); scales,
+ * h and the result as for qlin_linear_swiglu (h = bf16(bf16(silu(g)) * u) with
+ * g, u the projections rounded to bf16; W8A8 bit for bit with
+ * qlin_linear_swiglu).  Long inputs only: M >= 33 (else QLIN_ERR_UNSUPPORTED),
+ * I % 128 == 0 and K % 128 == 0 (QLIN_ERR_SHAPE); q_x / s_x staging required.
+ * One quantizer launch, then one tiled launch whose tiles hold 64 gate rows and
+ * the up rows with the same indices.  Validation, aliasing rules and error
+ * behaviour as qlin_linear_swiglu. */
+qlin_status qlin_linear_swiglu_packed(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
+                                      const void* gate_q_w_packed, const uint16_t* gate_s_w,
+                                      const void* up_q_w_packed, const uint16_t* up_s_w, int64_t I,
+                                      uint16_t* h, void* q_x, float* s_x, hipStream_t stream);
+
 /* Staging capacity of qlin_linear_noalloc: activation codes (M * K bytes) and
  * activation scales (M or M * K/128 floats). */
 #define QLIN_NOALLOC_MAX_CODE_BYTES  (16 << 20)

@@ -51,6 +51,7 @@ SIGNATURES = {
     "qlin_linear_noalloc": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P]),
     "qlin_pack_weights": (_S, [_S, _P, _I64, _I64, _P, _P]),
     "qlin_linear_packed": (_S, [_S, _P, _I64, _I64, _P, _I32, _S, _P, _P, _P]),
+    "qlin_linear_swiglu_packed": (_S, [_S, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P, _P, _P]),
     "qlin_status_string": (ctypes.c_char_p, [_S]),
     "qlin_abi_version": (_S, []),
     "qlin_last_hip_error": (_S, []),
@@ -277,6 +278,22 @@ def qlin_linear_packed(scheme, x, segments, out=OUT_BF16, q_x=None, s_x=None, st
     arr = segments_array(segments)
     _check(_lib.qlin_linear_packed(scheme, _ptr(x), M, K, arr, len(segments), out, _ptr(q_x), _ptr(s_x),
                                    _stream(stream)), "qlin_linear_packed")
+
+
+def qlin_linear_swiglu_packed(scheme, x, gate, up, h, q_x=None, s_x=None, stream=None):
+    """qlin_linear_swiglu for M >= 33 with gate and up as (packed q_w [I, K],
+    s_w) pairs from qlin_pack_weights; q_x / s_x staging required."""
+    M, K = _dims2(x, "x", 2)
+    (gq, gs), (uq, us) = gate, up
+    if gq.dim() != 2 or gq.shape[1] != K or tuple(uq.shape) != tuple(gq.shape):
+        raise ValueError("gate and up q_w must both be [I, K]")
+    I = gq.shape[0]
+    block = scheme == SCHEME_FP8_BLOCK
+    _args(("gate q_w", gq, I * K, 1), ("up q_w", uq, I * K, 1), ("gate s_w", gs, 2 * _sw_count(block, I, K), 2),
+          ("up s_w", us, 2 * _sw_count(block, I, K), 2), ("h", h, 2 * M * I, None), ("q_x", q_x, M * K, 1),
+          ("s_x", s_x, 4 * _sx_count(block, M, K), 4), ("x", x, 0, None))
+    _check(_lib.qlin_linear_swiglu_packed(scheme, _ptr(x), M, K, _ptr(gq), _ptr(gs), _ptr(uq), _ptr(us), I, _ptr(h),
+                                          _ptr(q_x), _ptr(s_x), _stream(stream)), "qlin_linear_swiglu_packed")
 
 
 def qlin_linear_noalloc(scheme, x, segments, out=OUT_BF16, stream=None):

@@ -57,7 +57,7 @@ __device__ __forceinline__ void pdma4(__amdgpu_buffer_rsrc_t r, void* dst, int v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, voff, 0, 0, 0);
 }
 
-template <int V, int BM, int KG>
+template <int V, int BM, int KG, bool SG>
 __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, SegmentArgs sa, int M, int K, int mode,
     int tiles_m, int tiles_n) {
@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t L0[KG * BST], L1[KG * BST], L2[KG * BST], L3[KG * BST];
     // the epilogue's scales, copied straight into LDS (raw bf16 row scales, f32
     // token scales); not used by block FP8
-    __shared__ __attribute__((aligned(16))) uint16_t s_w_raw[BLK ? 2 : kPBN];
+    // (SwiGLU: the gate rows' scales in [0, 64), the up rows' in [128, 192))
+    __shared__ __attribute__((aligned(16))) uint16_t s_w_raw[BLK ? 2 : SG ? 2 * kPBN : kPBN];
     __shared__ __attribute__((aligned(16))) float s_x_t[BLK ? 1 : BM];
     // block FP8: each stage's token scales s_x[m][s] ride a ring of four more
     // distinct arrays beside the token copies; wavefronts with no tokens to
@@ -95,24 +96,30 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     const int b = blockIdx.x;
     const int t = (ntiles & 7) ? b : ((b & 7) * (ntiles >> 3) + (b >> 3));
     int panel = __builtin_amdgcn_readfirstlane(t / tiles_m), seg = 0;
+    if constexpr (!SG) {
 #pragma unroll
-    for (int i = 0; i + 1 < kMaxSegments; ++i) {
-        const int np = (sa.start[i + 1] - sa.start[i]) / kPBN;   // segment widths are multiples of 128
-        if (seg == i && i + 1 < sa.nseg && panel >= np) {
-            panel -= np;
-            seg = i + 1;
+        for (int i = 0; i + 1 < kMaxSegments; ++i) {
+            const int np = (sa.start[i + 1] - sa.start[i]) / kPBN;   // segment widths are multiples of 128
+            if (seg == i && i + 1 < sa.nseg && panel >= np) {
+                panel -= np;
+                seg = i + 1;
+            }
         }
     }
+    // SwiGLU (segment 0 = gate, 1 = up, both [I, K], y = h [M, I]): a tile's
+    // 128 rows are 64 gate rows (wavefronts 0, 1) and the up rows with the same
+    // indices (wavefronts 2, 3)
+    const bool upw = SG && wave >= 2;
     // (selects over the statically loaded argument entries: no dependent scalar load)
-    const uint8_t* __restrict__ wp = pick_ptr(sa.w, seg);
-    const uint16_t* __restrict__ sw = pick_ptr(sa.sw, seg);
-    void* __restrict__ y = pick_ptr(sa.y, seg);
-    const int N = pick_int(sa.start + 1, seg) - pick_int(sa.start, seg);
-    const int n0 = panel * kPBN;
+    const uint8_t* __restrict__ wp = SG ? (upw ? sa.w[1] : sa.w[0]) : pick_ptr(sa.w, seg);
+    const uint16_t* __restrict__ sw = SG ? (upw ? sa.sw[1] : sa.sw[0]) : pick_ptr(sa.sw, seg);
+    void* __restrict__ y = SG ? sa.y[0] : pick_ptr(sa.y, seg);
+    const int N = SG ? sa.start[1] : pick_int(sa.start + 1, seg) - pick_int(sa.start, seg);
+    const int n0 = panel * (SG ? kPBN / 2 : kPBN);
     const int m0 = __builtin_amdgcn_readfirstlane((t % tiles_m) * BM);
 
     // this wavefront's 32-row weight block: 32 K bytes, 4 KB per stage
-    const int rb = (n0 >> 5) + wave;
+    const int rb = (n0 >> 5) + (SG ? (wave & 1) : wave);
     const __amdgpu_buffer_rsrc_t da = uniform_rsrc(wp + (int64_t)rb * 32 * K, 32 * K);
     const __amdgpu_buffer_rsrc_t db = uniform_rsrc(qx + (int64_t)m0 * K, min(BM, M - m0) * K);
     const int nk = K >> 7;
@@ -276,9 +283,12 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     // covers them; no register waits for them): wavefront 0 of group 0 copies
     // the 128 row scales (256 bytes), wavefront 1 the BM token scales (tokens
     // past M read as zero and are never stored)
-    if (!BLK && grp == 0 && wave == 0) {
-        const __amdgpu_buffer_rsrc_t ds = uniform_rsrc(sw + n0, kPBN * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ds, (__attribute__((address_space(3))) void*)s_w_raw, 4, 4 * lane, 0, 0, 0);
+    if (!BLK && grp == 0 && (wave == 0 || (SG && wave == 2))) {
+        // SwiGLU: 64 gate scales (wavefront 0) and 64 up scales (wavefront 2);
+        // the other half of each copy reads zeros
+        const __amdgpu_buffer_rsrc_t ds = uniform_rsrc(sw + n0, SG ? kPBN : kPBN * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ds, (__attribute__((address_space(3))) void*)(s_w_raw + (upw ? kPBN : 0)), 4,
+                                                 4 * lane, 0, 0, 0);
     } else if (!BLK && grp == 0 && wave == 1) {
         const __amdgpu_buffer_rsrc_t ds = uniform_rsrc(sx + m0, min(BM, M - m0) * 4);
 #pragma unroll
@@ -349,7 +359,59 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     }
 
     // Epilogue.  Lane l, element e of token tile i: weight row
-    // n0 + 32 w + 8 (e / 4) + 4 (l / 32) + e % 4, token m0 + 32 i + l % 32.
+    // n0 + 32 w + 8 (e / 4) + 4 (l / 32) + e % 4, token m0 + 32 i + l % 32
+    // (SwiGLU: gate / up row n0 + 32 (w % 2) + ...).  The scaled f32 output:
+    auto outv = [&](int i, int e) -> float {
+        if constexpr (BLK) {
+            return acc[i][e];                    // scaled per block in the loop
+        } else {
+            const int nl = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            const float f = s_x_t[BLK ? 0 : i * 32 + (lane & 31)] * bf16_lo(s_w_raw[SG && nl >= 64 ? nl + 64 : nl]);
+            if constexpr (V == VAR_INT8) return (float)acc[i][e] * f;
+            else return acc[i][e] * f;
+        }
+    };
+    if constexpr (SG) {
+        // the gate wavefronts' outputs go to LDS (wavefront 0 to L2, 1 to L3,
+        // free after the partial sums went through L0 / L1); the up wavefront
+        // with the same rows (2, 3) forms h = swiglu(g, u) for them, staged in
+        // L0 / L1 as BM rows of 64 bf16, then written as 16-byte row pieces
+        if (KG == 2) __syncthreads();            // group 0 has read the partial sums
+        float* gx = reinterpret_cast<float*>((wave & 1) ? L3 : L2) + lane;
+        if (grp == 0 && wave < 2) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) gx[(i * 16 + e) * 64] = outv(i, e);
+        }
+        __syncthreads();
+        constexpr int HP = kPBN + 16;           // 64 bf16 + 16 bytes per staged row
+        auto hrow = [&](int r) { return r < BM / 2 ? L0 + r * HP : L1 + (r - BM / 2) * HP; };
+        if (grp == 0 && wave >= 2) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int ml = i * 32 + (lane & 31);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint16_t hv[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) hv[k] = swiglu_bf16(gx[(i * 16 + 4 * g + k) * 64], outv(i, 4 * g + k));
+                    const int jl = (wave - 2) * 32 + 8 * g + 4 * half;
+                    *reinterpret_cast<v2u*>(hrow(ml) + jl * 2) =
+                        v2u{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
+                }
+            }
+        }
+        __syncthreads();
+        for (int id = tid; id < BM * 8; id += kPGT * KG) {
+            const int row = id >> 3, c = id & 7;
+            const int m = m0 + row;
+            if (m < M)
+                *reinterpret_cast<v4u*>(static_cast<uint16_t*>(y) + (int64_t)m * N + n0 + 8 * c) =
+                    *reinterpret_cast<const v4u*>(hrow(row) + 16 * c);
+        }
+        return;
+    }
     if (mode == OUT_BF16) {
         // a quarter of the tile's token rows in each ring array (free: the
         // partial sums went through L0 / L1 before the barrier below them)
@@ -437,15 +499,27 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
     }
 }
 
+// weight panels of a call: 128 rows of the segments, or (SwiGLU) 64 gate rows
+// with the matching up rows
+int64_t packed_panels(const SegmentArgs& sa, int mode) {
+    if (mode == OUT_SWIGLU) return sa.start[1] / (kPBN / 2);
+    int64_t tn = 0;
+    for (int i = 0; i < sa.nseg; ++i) tn += (sa.start[i + 1] - sa.start[i]) / kPBN;
+    return tn;
+}
+
 template <int V, int BM, int KG>
 hipError_t launch_packed_tile(const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M, int64_t K,
                               int mode, hipStream_t st) {
     const int64_t tm = (M + BM - 1) / BM;
-    int64_t tn = 0;
-    for (int i = 0; i < sa.nseg; ++i) tn += (sa.start[i + 1] - sa.start[i]) / kPBN;
+    const int64_t tn = packed_panels(sa, mode);
     if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_packed_kernel<V, BM, KG>), dim3((unsigned)(tm * tn)), dim3(kPGT * KG), 0, st, qx, sx, sa,
-                       (int)M, (int)K, mode, (int)tm, (int)tn);
+    if (mode == OUT_SWIGLU)
+        hipLaunchKernelGGL((gemm_packed_kernel<V, BM, KG, true>), dim3((unsigned)(tm * tn)), dim3(kPGT * KG), 0, st,
+                           qx, sx, sa, (int)M, (int)K, mode, (int)tm, (int)tn);
+    else
+        hipLaunchKernelGGL((gemm_packed_kernel<V, BM, KG, false>), dim3((unsigned)(tm * tn)), dim3(kPGT * KG), 0, st,
+                           qx, sx, sa, (int)M, (int)K, mode, (int)tm, (int)tn);
     return hipGetLastError();
 }
 
@@ -467,9 +541,7 @@ hipError_t launch_packed_shape(int shape, const uint8_t* qx, const float* sx, co
 // group, 64 KB of LDS) run two per CU instead.
 hipError_t launch_gemm_packed(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
                               int64_t K, int mode, hipStream_t st) {
-    int64_t panels = 0;
-    for (int i = 0; i < sa.nseg; ++i) panels += (sa.start[i + 1] - sa.start[i]) / kPBN;
-    const int64_t t128 = ((M + 127) / 128) * panels;
+    const int64_t t128 = ((M + 127) / 128) * packed_panels(sa, mode);
     const int shape = t128 > 256 ? 2 : t128 >= 192 ? 1 : 0;
     if (variant == VAR_INT8) return launch_packed_shape<VAR_INT8>(shape, qx, sx, sa, M, K, mode, st);
     if (variant == VAR_FP8_ROW) return launch_packed_shape<VAR_FP8_ROW>(shape, qx, sx, sa, M, K, mode, st);

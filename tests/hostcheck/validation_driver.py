@@ -30,6 +30,7 @@ SIG = {
     "qlin_linear": [S, P, I64, I64, P, I32, S, P, P, P],
     "qlin_linear_packed": [S, P, I64, I64, P, I32, S, P, P, P],
     "qlin_pack_weights": [S, P, I64, I64, P, P],
+    "qlin_linear_swiglu_packed": [S, P, I64, I64, P, P, P, P, I64, P, P, P, P],
     "qlin_linear_weight_only": [S, P, I64, I64, P, I32, S, P],
     "qlin_linear_swiglu": [S, P, I64, I64, P, P, P, P, I64, P, P, P, P],
 }
@@ -122,6 +123,10 @@ assert call("qlin_linear_packed", 0, x, 64, 256, three, 3, 0, A + 0xA000000, A +
 assert call("qlin_linear_packed", 2, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == OK
 assert call("qlin_linear_packed", 9, x, 64, 256, wide, 2, 0, A + 0xA000000, A + 0xB000000, None) == UNSUP
 assert call("qlin_pack_weights", 1, A, 256, 384, A + 0x1000000, None) == OK
+assert call("qlin_linear_swiglu_packed", 2, x, 64, 256, A + 0x1000000, A + 0x2000000, A + 0x4000000, A + 0x5000000, 128,
+            A + 0x6000000, A + 0xA000000, A + 0xB000000, None) == OK
+assert call("qlin_linear_swiglu_packed", 0, x, 16, 256, A + 0x1000000, A + 0x2000000, A + 0x4000000, A + 0x5000000,
+            128, A + 0x6000000, A + 0xA000000, A + 0xB000000, None) == UNSUP
 assert call("qlin_pack_weights", 1, A, 256, 384, A + 0x100, None) == ALIAS
 assert call("qlin_pack_weights", 0, A, 200, 384, A + 0x1000000, None) == SHAPE
 assert call("qlin_quant_act_fp8", x, 4, 256, 64, A + 0x1000000, A + 0x2000000, None) == SHAPE
@@ -178,6 +183,7 @@ for it in range(20000):
     elif fn == 7:
         call("qlin_pack_weights", scheme, ptr(), N, K, ptr(), None)
     else:
-        call("qlin_linear_swiglu", scheme, ptr(), M, K, ptr(), ptr(), ptr(), ptr(), size(), ptr(), ptr(), ptr(), None)
+        call(rng.choice(["qlin_linear_swiglu", "qlin_linear_swiglu_packed"]), scheme, ptr(), M, K, ptr(), ptr(), ptr(),
+             ptr(), size(), ptr(), ptr(), ptr(), None)
 
 print(f"hostcheck: {calls} calls, {lib.qlin_hostcheck_launches()} reached a launcher, no sanitizer report")

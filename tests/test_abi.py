@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libqlin.so"
         assert n in Q.SIGNATURES, f"{n} has no binding signature"
@@ -244,6 +244,21 @@ def test_linear_packed_validation():
     assert lp(1, x, 64, 256, segs, 2, Q.OUT_I32, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED
     assert lp(0, x, 0, 256, segs, 2, 0, qx, sx, None) == Q.QLIN_OK                 # M == 0
     assert lp(0, x, 64, 256, segs, 2, 0, A + 0x1000000 + 64, sx, None) == Q.QLIN_ERR_ALIAS   # q_x in q_w
+
+
+def test_linear_swiglu_packed_validation():
+    sg = L.qlin_linear_swiglu_packed
+    x, gq, gs, uq, us, h = A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x5000000
+    qx, sx = A + 0x6000000, A + 0x7000000
+    assert sg(9, x, 64, 256, gq, gs, uq, us, 128, h, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED
+    assert sg(0, x, 0, 256, gq, gs, uq, us, 128, h, qx, sx, None) == Q.QLIN_OK         # M == 0
+    assert sg(0, x, 64, 256, gq, gs, uq, us, 0, h, qx, sx, None) == Q.QLIN_OK          # I == 0
+    assert sg(0, x, 32, 256, gq, gs, uq, us, 128, h, qx, sx, None) == Q.QLIN_ERR_UNSUPPORTED   # M <= 32
+    assert sg(0, x, 64, 256, gq, gs, uq, us, 64, h, qx, sx, None) == Q.QLIN_ERR_SHAPE   # I % 128
+    assert sg(1, x, 64, 272, gq, gs, uq, us, 128, h, qx, sx, None) == Q.QLIN_ERR_SHAPE  # K % 128
+    assert sg(0, x, 64, 256, gq, gs, uq, us, 128, h, None, None, None) == Q.QLIN_ERR_NULL   # staging required
+    assert sg(0, x, 64, 256, None, gs, uq, us, 128, h, qx, sx, None) == Q.QLIN_ERR_NULL
+    assert sg(0, x, 64, 256, gq, gs, uq, us, 128, uq + 256, qx, sx, None) == Q.QLIN_ERR_ALIAS   # h in up
 
 
 def test_library_has_no_unresolved_internal_symbols():

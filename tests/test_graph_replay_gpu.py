@@ -66,6 +66,19 @@ def build(torch):
         sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32)
         outs += [qx, sx]
         calls.append(lambda s=scheme, x=x, segs=segs, qx=qx, sx=sx: Q().qlin_linear_packed(s, x, segs, q_x=qx, s_x=sx))
+    # SwiGLU on packed weights, block FP8
+    x = dev(W.x_bf16(9975, 100, 256))
+    pair = []
+    for j in range(2):
+        pw = torch.empty((256, 256), dtype=torch.uint8, device="cuda")
+        Q().qlin_pack_weights(FP8B, dev(W.w_e4m3(9976 + j, 256, 256)), pw)
+        pair.append((pw, dev(W.scale_bf16(9978 + j, (2, 2), 1e-4, 5e-4))))
+    h = empty(torch, (100, 256), torch.int16)
+    qx = empty(torch, (100, 256), torch.uint8)
+    sx = empty(torch, (100, 2), torch.float32)
+    outs += [h, qx, sx]
+    calls.append(lambda x=x, p=pair, h=h, qx=qx, sx=sx: Q().qlin_linear_swiglu_packed(FP8B, x, p[0], p[1], h, q_x=qx,
+                                                                                        s_x=sx))
     for i, (M, K) in enumerate([(1, 4096), (4, 1024), (40, 512)]):
         x = dev(W.x_bf16(9980 + i, M, K))
         gate = (dev(W.w_int8(9985 + i, 256, K)), dev(W.scale_bf16(9988 + i, 256, 1e-4, 5e-4)))

@@ -222,3 +222,71 @@ def test_linear_packed_refuses_small_m():
     with pytest.raises(Q().QlinError):
         Q().qlin_pack_weights(9, pw, torch.empty_like(pw))
     assert (host(y).view(np.uint8) == 0x3C).all()      # nothing launched
+
+
+# ---- SwiGLU on packed weights ---------------------------------------------
+
+SG_CASES = [
+    # (M, K, I): 128 x 64 tiles (two K groups), ragged tails, 128 x 128 with two
+    # K groups (192 tiles), with one K group (past 256 tiles)
+    (33, 128, 128),
+    (200, 1024, 384),
+    (150, 512, 4096),
+    (256, 128, 6144),
+    (300, 256, 8192),
+]
+
+
+def run_swiglu_packed(scheme, x, pair):
+    torch = torch_mod()
+    M, K = x.shape
+    I = pair[0][0].shape[0]
+    h = empty(torch, (M * I * 2 + 64,), torch.uint8, fill=0xFF)
+    qx = empty(torch, (M, K), torch.uint8, fill=0x55)
+    sx = empty(torch, (M, K // 128) if scheme == FP8B else (M,), torch.float32, fill=0x55)
+    packed = []
+    for qw, sw in pair:
+        pw = empty(torch, (I, K), torch.uint8)
+        Q().qlin_pack_weights(scheme, dev(qw), pw)
+        packed.append((pw, dev(sw)))
+    Q().qlin_linear_swiglu_packed(scheme, dev(x), packed[0], packed[1], h, q_x=qx, s_x=sx)
+    raw = host(h)
+    assert (raw[M * I * 2:] == 0xFF).all(), "guard band overwritten"
+    return raw[:M * I * 2].view(np.uint16).reshape(M, I)
+
+
+@pytest.mark.parametrize("scheme", [W8A8, FP8R, FP8B])
+@pytest.mark.parametrize("M,K,I", SG_CASES)
+def test_swiglu_packed_matches_oracle(scheme, M, K, I):
+    from test_parity_swiglu_gpu import check, make_pair, run
+    x = W.x_bf16(8900 + M + K, M, K)
+    gate, up = make_pair(scheme, 8910 + I, I, K)
+    h = run_swiglu_packed(scheme, x, (gate, up))
+    check(scheme, x, gate, up, h, f"swiglu packed scheme {scheme} M={M} K={K} I={I}")
+    if scheme == W8A8:
+        # the row-major launch: same int32 sums and epilogue, so the same h
+        h_rm, _, _ = run(scheme, x, gate, up, True)
+        assert np.array_equal(h, h_rm)
+
+
+@pytest.mark.parametrize("scheme,K,I", [(W8A8, 4096, 14336), (FP8R, 4096, 14336), (FP8B, 4096, 12288)])
+def test_swiglu_packed_8b_gate_up_512_tokens(scheme, K, I):
+    from test_parity_swiglu_gpu import check, make_pair
+    M = 512
+    x = W.x_bf16(8950 + I, M, K)
+    gate, up = make_pair(scheme, 8960 + I, I, K)
+    check(scheme, x, gate, up, run_swiglu_packed(scheme, x, (gate, up)), f"8B gate/up scheme {scheme}")
+
+
+def test_swiglu_packed_refuses_small_m():
+    torch = torch_mod()
+    K, I = 256, 128
+    x = dev(W.x_bf16(8990, 32, K))
+    pw = dev(W.w_int8(8991, I, K))
+    sw = dev(W.scale_bf16(8992, (I,)))
+    h = empty(torch, (32, I), torch.int16, fill=0x3C)
+    qx, sx = empty(torch, (32, K), torch.uint8), empty(torch, (32,), torch.float32)
+    with pytest.raises(Q().QlinError):
+        Q().qlin_linear_swiglu_packed(W8A8, x, (pw, sw), (pw, sw), h, q_x=qx, s_x=sx)
+    assert (host(h).view(np.uint8) == 0x3C).all()      # nothing launched
+
