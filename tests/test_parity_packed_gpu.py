@@ -104,6 +104,7 @@ CASES = [
     (97, 4096, [640, 128, 512, 256]),       # four segments, long K
     (1100, 256, [2048, 2048]),              # past 256 tiles of 128 x 128 (9 x 32): one K group, ragged 76
     (2000, 128, [2304]),                    # one K group (16 x 18 tiles), one K stage only
+    (600, 256, [8192, 8192]),               # one K group, 5 x 128 tiles, ragged 88
 ]
 
 
