@@ -1,7 +1,8 @@
 // Long-input products with the weights stored in the matrix-core operand
 // order (W8A8 model card, "Loading": inputs of more than 32 rows are rounded
 // per row and multiplied in int8 with int32 sums; the FP8 rowwise scheme the
-// same way on E4M3 codes).
+// same way on E4M3 codes; Qwen3 8B FP8 card, "Loading": block-scaled E4M3
+// with per-128-input activation scales).
 //
 // Packed layout ("operand order").  q_w [N, K] is cut into blocks of 32 rows
 // and K-slices of S bytes (S = 32 for int8, 64 for E4M3: one MFMA's K); each
@@ -11,24 +12,30 @@
 //     = q_w[32 rb + l % 32][S s + (S / 2) (l / 32) + 16 h + b],   b < 16.
 // (v_mfma_i32_32x32x32_i8 takes row l % 32, bytes 16 (l / 32) .. + 16 of a
 // 32-byte slice from lane l; v_mfma_f32_32x32x64_f8f6f4 bytes 32 (l / 32) ..
-// + 32 of a 64-byte slice.)  In both schemes a 128-byte K stage of one block
-// is 4 KB of consecutive units.
+// + 32 of a 64-byte slice.)  In both code types a 128-byte K stage of one
+// block is 4 KB of consecutive units.
 //
 // Why: a 128 x 64 output tile per CU (the o and down projections at 512
 // tokens, whose outputs leave no larger tile for 256 CUs) moves 72 KB through
 // LDS per 256 MFMA cycles when both operands are staged there -- 288 B/clk,
 // above the LDS rate.  With the weights in operand order each wavefront loads
 // its own 32 weight rows straight into registers, 1 KB contiguous per load,
-// and only the tokens go through LDS (40 KB per 256 cycles).
+// and only the tokens go through LDS (40 KB per 256 cycles).  The loop is then
+// bound by its load instructions rather than by LDS or the matrix cores.
 //
 // Tile: 128 weight rows x BM tokens (BM = 64 or 128); KG = 1 or 2 K groups of
 // four wavefronts (group g multiplies stages g, g + KG, ...), wavefront w of a
-// group owns weight rows [32 w, 32 w + 32) and all BM tokens.  Tokens: a ring of four
-// LDS buffers per group filled by direct copies (buffer_load ... lds) three
-// steps ahead, 16-byte chunks XOR-swizzled by row; weights: a ring of four
-// register sets loaded three steps ahead.  One barrier per step.  Group 1 adds
-// its sums into group 0's through LDS; the epilogue is the rowwise one of the
-// row-major tiled product (same f32 order, bf16 staged through LDS).
+// group owns weight rows [32 w, 32 w + 32) and all BM tokens.  Tokens: a ring
+// of four LDS buffers per group filled by direct copies (buffer_load ... lds)
+// three steps ahead, 16-byte chunks XOR-swizzled by row; weights: a ring of
+// four register sets loaded three steps ahead.  One barrier per step.  Group
+// 1 adds its sums into group 0's through LDS; the epilogue is the rowwise one
+// of the row-major tiled product (same f32 order, bf16 staged through LDS).
+// Block FP8: a 128-row tile lies in one 128-row scale block, so a stage (one
+// 128-input block) has one weight scale; each token tile's partial product is
+// scaled by s_x[m][s] * s_w[n0 / 128][s] into the f32 accumulator.  SwiGLU
+// (SG): the tile's rows are 64 gate rows and the up rows with the same
+// indices, and the gate outputs reach the up wavefronts through LDS.
 #include <type_traits>
 
 #include "qlin_device.h"

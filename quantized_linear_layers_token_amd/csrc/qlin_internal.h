@@ -65,10 +65,11 @@ int large_tile_config(int variant, int64_t M, const SegmentArgs& sa);
 hipError_t launch_gemm_large(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
                              int64_t K, int mode, hipStream_t st);
 
-// The tiled product on weights in the matrix-core operand order (int8 and FP8
-// rowwise; every segment's width a multiple of 128, K % 128 == 0): one launch
-// over every segment.  launch_pack_weights writes that order from row-major
-// codes ([N, K], N % 128 == 0, K % 128 == 0).
+// The tiled product on weights in the matrix-core operand order (every scheme;
+// every segment's width a multiple of 128, K % 128 == 0): one launch over every
+// segment, or with mode OUT_SWIGLU over the gate (segment 0) / up (segment 1)
+// pair into h.  launch_pack_weights writes that order from row-major codes
+// ([N, K], N % 128 == 0, K % 128 == 0; block FP8 codes as E4M3, VAR_FP8_ROW).
 hipError_t launch_gemm_packed(int variant, const uint8_t* qx, const float* sx, const SegmentArgs& sa, int64_t M,
                               int64_t K, int mode, hipStream_t st);
 hipError_t launch_pack_weights(int variant, const uint8_t* w, int64_t N, int64_t K, uint8_t* p, hipStream_t st);
