@@ -362,8 +362,7 @@ def prefill_layer_set(torch, Q, W, variant, M, layers, dev, seed0):
                 packed.linear_packed(scheme, x, psegs, qx=q, sx=s)
                 packed_sg.linear_packed(scheme, x, psegs, qx=q, sx=s)
                 packed.outputs += [y for _, _, y in segs]
-    packed.sg_launcher = packed_sg
-    return full, prod, fused, swiglu, packed, packed_all, ops, keep
+    return full, prod, fused, swiglu, packed, packed_sg, packed_all, ops, keep
 
 
 def layer_set(torch, Q, W, scheme, shapes, M, layers, dev, seed0):
@@ -551,16 +550,16 @@ def main():
         copy_calibration()
         for variant in args.prefill_variants.split(","):
             for M in (int(m) for m in args.prefill_m.split(",")):
-                _, _, fused, _, packed, packed_all, ops, keep = prefill_layer_set(
+                _, _, fused, _, packed, packed_sg, packed_all, ops, keep = prefill_layer_set(
                     torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
-                run = packed.sg_launcher if args.prefill_packed else fused
+                run = packed_sg if args.prefill_packed else fused
                 torch.cuda.synchronize()
                 for _ in range(3):
                     run.run()
                 torch.cuda.synchronize()
                 log(f"prefill workload {variant}{' packed' if run is packed else ''}: M={M}, 4 layers, "
                     f"{len(run.calls)} calls per pass x3, {ops} ops per pass")
-                del keep, fused, packed, packed_all, run
+                del keep, fused, packed, packed_sg, packed_all, run
         return
     if args.smallm_workload:
         copy_calibration()
@@ -773,7 +772,7 @@ def main():
         for variant, peak in (("int8", MFMA_INT8_PEAK_TOPS), ("fp8_row", MFMA_FP8_PEAK_TOPS),
                               ("fp8_block", MFMA_FP8_PEAK_TOPS)):
             for M in (512, 1024):
-                full, prod, fused, swiglu, packed, packed_all, ops, keep = prefill_layer_set(
+                full, prod, fused, swiglu, packed, packed_sg, packed_all, ops, keep = prefill_layer_set(
                     torch, Q, W, variant, M, 4, dev, {"int8": 300, "fp8_row": 400, "fp8_block": 500}[variant] + M)
                 f_full = capture(torch, full.run, use_graph)
                 f_prod = capture(torch, prod.run, use_graph)
@@ -781,7 +780,7 @@ def main():
                 f_sg = capture(torch, swiglu.run, use_graph)
                 f_pk = capture(torch, packed.run, use_graph)
                 f_pa = capture(torch, packed_all.run, use_graph)
-                f_ps = capture(torch, packed.sg_launcher.run, use_graph)
+                f_ps = capture(torch, packed_sg.run, use_graph)
                 t_full = time_warm(torch, f_full)
                 t_prod = time_warm(torch, f_prod)
                 t_fused = time_warm(torch, f_fused)
@@ -823,7 +822,7 @@ def main():
                 secondary[key]["tops_packed_all_swiglu"] = round(ops / (t_ps * 1e-3) / 1e12, 1)
                 secondary[key]["frac_packed_all_swiglu"] = round(ops / (t_ps * 1e-3) / 1e12 / peak, 4)
                 log(f"{key}: {secondary[key]}")
-                del keep, full, prod, fused, swiglu, packed, packed_all, f_full, f_prod, f_fused, f_sg, f_pk, f_pa, f_ps
+                del keep, full, prod, fused, swiglu, packed, packed_sg, packed_all, f_full, f_prod, f_fused, f_sg, f_pk, f_pa, f_ps
                 torch.cuda.synchronize()
 
     cpu = None

@@ -1,6 +1,6 @@
 """GPU parity of the packed-weight path: qlin_pack_weights against the layout
-definition (a numpy reshape/transpose of the row-major codes, written from the
-layout formula in include/qlin.h), and qlin_linear_packed against the CPU
+definition (packed_layout.packed_reference, pinned to the formula in
+include/qlin.h by test_packed_layout.py), and qlin_linear_packed against the CPU
 oracle -- W8A8 bit for bit (same int32 sums, same f32 epilogue order; the
 int32 accumulator output exactly), FP8 rowwise and block FP8 within the FP8
 tolerance -- on 64- and 128-token tiles, one and two K groups, ragged token
@@ -12,6 +12,7 @@ import pytest
 import oracle as O
 import workloads as W
 from gpu_helpers import assert_within_tol, dev, empty, host, torch_mod
+from packed_layout import packed_reference
 
 pytestmark = pytest.mark.gpu
 BF16, I32, F32 = 0, 1, 2
@@ -21,33 +22,6 @@ W8A8, FP8R, FP8B = 0, 1, 2
 def Q():
     import quantized_linear_layers_token_amd as q
     return q
-
-
-def packed_reference(w: np.ndarray, S: int) -> np.ndarray:
-    """packed[((rb * (K/S) + s) * H + h) * 1024 + 16 l + b] =
-    w[32 rb + l % 32][S s + (S/2)(l / 32) + 16 h + b], H = S / 32, as a reshape."""
-    N, K = w.shape
-    H = S // 32
-    # axes of w: rb, r (= l % 32), s, half (= l / 32), h, b
-    v = w.reshape(N // 32, 32, K // S, 2, H, 16)
-    # packed order: rb, s, h, half, r, b   (l = 32 half + r)
-    return np.ascontiguousarray(v.transpose(0, 2, 4, 3, 1, 5)).reshape(-1)
-
-
-def test_packed_reference_is_a_permutation_with_the_stated_entries():
-    # the reshape above against the formula, entry by entry, on a small case
-    rng = np.random.default_rng(5)
-    for S in (32, 64):
-        N, K = 64, 128
-        w = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
-        p = packed_reference(w, S)
-        H = S // 32
-        for _ in range(2000):
-            rb, s, h = rng.integers(0, N // 32), rng.integers(0, K // S), rng.integers(0, H)
-            l, b = rng.integers(0, 64), rng.integers(0, 16)
-            got = p[((rb * (K // S) + s) * H + h) * 1024 + 16 * l + b]
-            assert got == w[32 * rb + l % 32, S * s + (S // 2) * (l // 32) + 16 * h + b]
-        assert np.array_equal(np.sort(p), np.sort(w.reshape(-1)))
 
 
 @pytest.mark.parametrize("scheme,S", [(W8A8, 32), (FP8R, 64), (FP8B, 64)])
