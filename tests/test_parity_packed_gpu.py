@@ -147,6 +147,40 @@ def test_linear_packed_block_long_k():
         assert_within_tol(y, exact(FP8B, qx_ref, sx_ref, qw, sw), f"packed block K={K}")
 
 
+@pytest.mark.parametrize("scheme", [W8A8, FP8B])
+def test_linear_packed_max_k(scheme):
+    # K = QLIN_MAX_K: 1024 stages, 4 MB per 32-row block descriptor, 1024 block scales per row
+    K = Q().MAX_K
+    M = 40
+    x = W.x_bf16(8470, M, K)
+    segs = packed_segments(scheme, 8471, [128], K)
+    qx_ref, sx_ref = oracle_quant(scheme, x)
+    (qw, sw, _), = segs
+    y, = run_packed(scheme, x, segs, BF16)
+    if scheme == W8A8:
+        assert np.array_equal(y, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
+    assert_within_tol(y, exact(scheme, qx_ref, sx_ref, qw, sw), f"packed K={K}")
+
+
+def test_linear_packed_empty_segment_in_the_list():
+    # a zero-width segment between two others is skipped; the others' panels follow on
+    torch = torch_mod()
+    M, K = 70, 256
+    x = W.x_bf16(8480, M, K)
+    a = packed_segments(W8A8, 8481, [256], K)[0]
+    c = packed_segments(W8A8, 8482, [128], K)[0]
+    ya = empty(torch, (M, 256), torch.int16, fill=0x11)
+    yc = empty(torch, (M, 128), torch.int16, fill=0x11)
+    qx, sx = empty(torch, (M, K), torch.uint8), empty(torch, (M,), torch.float32)
+    none = torch.empty((0, K), dtype=torch.uint8, device="cuda")
+    Q().qlin_linear_packed(W8A8, dev(x), [(a[2], dev(a[1]), ya), (none, None, None), (c[2], dev(c[1]), yc)],
+                           q_x=qx, s_x=sx)
+    qx_ref, sx_ref = O.quant_act_int8(x)
+    for (qw, sw, _), y in ((a, ya), (c, yc)):
+        got = host(y).view(np.uint16)
+        assert np.array_equal(got, O.epilogue_f32_order(O.contract_int8(qx_ref, qw), sx_ref, sw))
+
+
 LLAMA = [("qkv", 4096, [4096, 1024, 1024]), ("o", 4096, [4096]), ("down", 14336, [4096])]
 QWEN3 = [("qkv", 4096, [4096, 1024, 1024]), ("o", 4096, [4096]), ("down", 12288, [4096]),
          ("gateup", 4096, [12288, 12288])]
@@ -251,6 +285,15 @@ def test_swiglu_packed_8b_gate_up_512_tokens(scheme, K, I):
     x = W.x_bf16(8950 + I, M, K)
     gate, up = make_pair(scheme, 8960 + I, I, K)
     check(scheme, x, gate, up, run_swiglu_packed(scheme, x, (gate, up)), f"8B gate/up scheme {scheme}")
+
+
+def test_swiglu_packed_block_odd_block_count():
+    # K / 128 = 33 blocks (odd): each stage's bf16 scale at an odd 2-byte offset of its row
+    from test_parity_swiglu_gpu import check, make_pair
+    M, K, I = 50, 33 * 128, 256
+    x = W.x_bf16(8980, M, K)
+    gate, up = make_pair(FP8B, 8981, I, K)
+    check(FP8B, x, gate, up, run_swiglu_packed(FP8B, x, (gate, up)), "swiglu packed block, 33 K blocks")
 
 
 def test_swiglu_packed_refuses_small_m():
