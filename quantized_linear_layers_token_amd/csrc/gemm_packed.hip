@@ -279,7 +279,8 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
 
     // Step kt multiplies stage gs(kt) from register set / buffer kt % 4 once
     // this wavefront's loads of it are complete (the loads of the two later
-    // stages may stay in flight: vmcnt <= 2 (4 + BW)) and every wavefront has
+    // stages may stay in flight: vmcnt <= twice one stage's count, 4 + BW, and
+    // two more for block FP8's scales) and every wavefront has
     // passed the barrier (so their copies of it are in LDS and nobody still
     // reads buffer (kt + 3) % 4), then issues stage gs(kt + 3) into set and
     // buffer (kt + 3) % 4.  The explicit s_barrier (no fence) leaves those
@@ -289,7 +290,8 @@ __global__ __launch_bounds__(kPGT * KG) void gemm_packed_kernel(
     // scales first (older than every stage load, so the first step's wait
     // covers them; no register waits for them): wavefront 0 of group 0 copies
     // the 128 row scales (256 bytes), wavefront 1 the BM token scales (tokens
-    // past M read as zero and are never stored)
+    // past M read as zero and are never stored); block FP8 loads its scales
+    // with each stage instead
     if (!BLK && grp == 0 && (wave == 0 || (SG && wave == 2))) {
         // SwiGLU: 64 gate scales (wavefront 0) and 64 up scales (wavefront 2);
         // the other half of each copy reads zeros
