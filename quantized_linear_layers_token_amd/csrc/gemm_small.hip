@@ -233,6 +233,36 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(
                     tx[t][1] = *reinterpret_cast<const v4u*>(tpw + (RT + t) * 2048 + rd_off1);
                 }
             }
+            if constexpr (V == VAR_FP8_BLOCK) {
+                // every tile's partial product of this step first, then the
+                // scaling: the MFMAs issue back to back instead of each waiting
+                // for the previous one's result to be read (steps past the
+                // wavefront's range multiplied zeros: factor 0, branch-free, so
+                // every path from an MFMA to its first read is the padded one)
+                v4f pp[RT][MT];
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const v4u w0 = ta[r][0], w1 = ta[r][1], x0 = tx[t][0], x1 = tx[t][1];
+                        const v8i a = v8i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+                        const v8i b = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                        pp[r][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                                   0, 0, 0);
+                    }
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const float fxv = FU ? fsc[min(r16, M - 1) * kSmallFusedGroups + min(s0 + u, s_end - 1)]
+                                             : fx[bi][u][t];
+                        const float f = s0 + u < s_end ? fxv * fw[bi][u][(SG && r >= RH) ? 1 : 0] : 0.0f;
+                        acc[r][t].x = __builtin_fmaf(pp[r][t].x, f, acc[r][t].x);
+                        acc[r][t].y = __builtin_fmaf(pp[r][t].y, f, acc[r][t].y);
+                        acc[r][t].z = __builtin_fmaf(pp[r][t].z, f, acc[r][t].z);
+                        acc[r][t].w = __builtin_fmaf(pp[r][t].w, f, acc[r][t].w);
+                    }
+            } else
 #pragma unroll
             for (int r = 0; r < RT; ++r)
 #pragma unroll
