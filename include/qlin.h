@@ -290,7 +290,7 @@ qlin_status qlin_linear_swiglu(qlin_scheme scheme, const uint16_t* x, int64_t M,
  * that each wavefront of the tiled kernel loads its weight rows straight into
  * the matrix-core operand registers, 1 KB contiguous per load, and only the
  * tokens pass through LDS.  q_w [N, K] is cut into blocks of 32 rows and
- * K-slices of S bytes (S = 32 for W8A8, 64 for FP8_ROWWISE); with H = S / 32:
+ * K-slices of S bytes (S = 32 for W8A8, 64 for the E4M3 schemes); with H = S / 32:
  *   packed[((rb * (K / S) + s) * H + h) * 1024 + 16 l + b]
  *     = q_w[32 rb + l % 32][S s + (S / 2) (l / 32) + 16 h + b],   l < 64, b < 16
  * (a permutation of the N * K bytes).
@@ -318,8 +318,10 @@ qlin_status qlin_pack_weights(qlin_scheme scheme, const void* q_w, int64_t N, in
  * then one tiled launch over every segment (128 weight rows x 64 or 128 tokens
  * per tile).  Validation, aliasing rules and error behaviour as qlin_linear.
  * Packing pays on projections whose outputs give each CU at most a 128 x 128
- * tile (q/k/v, o and down of an 8B model at 512-1024 tokens); the wide gate/up
- * projection runs faster row-major on the 256 x 256 tiles of qlin_linear. */
+ * tile (q/k/v, o and down of an 8B model at 512-1024 tokens); for W8A8 and
+ * FP8_ROWWISE the wide gate/up projection runs as fast row-major, on the
+ * 256 x 256 tiles of qlin_linear / qlin_linear_swiglu.  FP8_BLOCK has no such
+ * row-major tile and is faster packed on every projection. */
 qlin_status qlin_linear_packed(qlin_scheme scheme, const uint16_t* x, int64_t M, int64_t K,
                                const qlin_segment* segments, int32_t nseg, qlin_out out,
                                void* q_x, float* s_x, hipStream_t stream);
