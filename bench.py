@@ -77,6 +77,9 @@ def parse():
                          "projection M=16 N=K=4096 (32 weight copies) and the W8A8 Llama layer set at M=4, 16, "
                          "32 (4 layers each), one qlin_linear call per input, three eager passes each; "
                          "prints no JSON")
+    ap.add_argument("--smallm-schemes", default="int8",
+                    help="comma list of int8, fp8_row, fp8_block for --smallm-workload (int8 also runs the "
+                         "16 x 4096 x 4096 projection; fp8_block uses the Qwen3-8B shapes)")
     return ap.parse_args()
 
 
@@ -563,6 +566,23 @@ def main():
         return
     if args.smallm_workload:
         copy_calibration()
+        schemes = args.smallm_schemes.split(",")
+        for sname in schemes:
+            if sname == "int8":
+                continue
+            scheme = Q.SCHEME_FP8_ROWWISE if sname == "fp8_row" else Q.SCHEME_FP8_BLOCK
+            shapes = W.QWEN3_8B if sname == "fp8_block" else W.LLAMA_8B
+            for M in (4, 16, 32):
+                Lr, nbytes, ops, keep = layer_set(torch, Q, W, scheme, shapes, M, 4, dev, 600 + M)
+                torch.cuda.synchronize()
+                for _ in range(3):
+                    Lr.run()
+                torch.cuda.synchronize()
+                log(f"small-M workload: {sname} layer M={M}, 4 layers, {len(Lr.calls)} calls per pass x3, "
+                    f"{nbytes} algorithmic bytes per pass")
+                del Lr, keep
+        if "int8" not in schemes:
+            return
         gen = torch.Generator(device=dev)
         gen.manual_seed(1)
         c1 = Launcher(Q, torch)
