@@ -166,17 +166,23 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
         }
     }
 
-    // The lane's slices of the rounded token stay in registers, except for FP8
-    // rowwise rows longer than 8 KiB (XL): there each slice is read from the
-    // LDS copy where it is used and a wavefront takes one row, which keeps the
-    // kernel at or below 128 registers (four wavefronts per SIMD, every row of
-    // the launch in flight).  Measured over the Llama-3.1-8B decode step: FP8
-    // rowwise 1.392 -> 1.376 ms; the same form made int8 slower (1.372 ->
-    // 1.387 ms) and block FP8 slower (1.534 -> 1.556 ms on Qwen3-8B: 144
-    // registers, three wavefronts per SIMD).
-    constexpr bool XL = KC > 8 && V == VAR_FP8_ROW;
-    v4u xr[XL ? 1 : SL];
-    if constexpr (!XL) {
+    // The lane's slices of the rounded token stay in registers (int8, FP8
+    // rowwise), except for FP8 rowwise rows longer than 8 KiB (XL): there each
+    // slice is read from the LDS copy where it is used and a wavefront takes
+    // one row, which keeps the kernel at or below 128 registers (four
+    // wavefronts per SIMD, every row of the launch in flight).  Measured over
+    // the Llama-3.1-8B decode step: FP8 rowwise 1.392 -> 1.376 ms; the same form
+    // made int8 slower (1.372 -> 1.387 ms).  Block FP8 reads its (permuted)
+    // slices from LDS at every row length (TL), takes the XL form for rows up
+    // to 4 KiB (one row per wavefront: 42 registers, eight wavefronts per SIMD
+    // instead of six) and keeps two rows per wavefront in turn beyond 8 KiB;
+    // its partial products are consumed two at a time.  Qwen3-8B block decode
+    // 1.541-1.556 -> 1.502-1.507 ms per token (alternated on one box, outputs
+    // bit-identical).
+    constexpr bool XL = (KC > 8 && V == VAR_FP8_ROW) || (KC <= 4 && V == VAR_FP8_BLOCK);
+    constexpr bool TL = XL || V == VAR_FP8_BLOCK;
+    v4u xr[TL ? 1 : SL];
+    if constexpr (!TL) {
 #pragma unroll
         for (int j = 0; j < SL; ++j) {
             const int o = slot(j);
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     };
     float gx[NF];                  // block FP8: s_x of group l (and 64 + l)
     if constexpr (V == VAR_FP8_BLOCK) {
-        if constexpr (!XL) {
+        if constexpr (!TL) {
 #pragma unroll
             for (int j = 0; j < SL; ++j) xr[j] = bperm(xr[j]);
         }
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     // the lane's token slice j (block FP8: the slice lane 4 (l % 16) + l / 16 loaded)
     const int tlane = V == VAR_FP8_BLOCK ? 4 * (lane & 15) + (lane >> 4) : lane;
     auto tok = [&](int j) -> v4u {
-        if constexpr (XL) {
+        if constexpr (TL) {
             const int o = j * kWave + tlane;
             return (o < k16) ? *reinterpret_cast<const v4u*>(xq + o * 16) : v4u{0, 0, 0, 0};
         } else {
@@ -251,6 +257,9 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
                     const int g = (8 * q + ((lane & 15) >> 1)) & 63;   // group 8 q + i / 2, in register q / 8
                     const float fg = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * g, __float_as_int(f[q / 8])));
                     a = __builtin_fmaf(mfma16_diag(p, lane), fg, a);
+                    // at most two partial products in flight: nothing is
+                    // scheduled across this point
+                    if (q % 2 == 1) __builtin_amdgcn_sched_barrier(0);
                 }
                 facc[r] = wave_sum_f32(a);
             }
@@ -339,7 +348,8 @@ void decode_launch_shape(int variant, int64_t ntot, int64_t K, int* R, int* grid
     const int64_t kc = (K + 1023) / 1024;
     *R = (kc > 4 && kc <= 8) ? 2 : 1;
     // one row per wavefront up to 4 KiB and, for FP8 rowwise, past 8 KiB (the
-    // kernel's long-row form handles exactly one), else two per wavefront
+    // kernel's XL form -- FP8 rowwise past 8 KiB, block FP8 up to 4 KiB --
+    // handles exactly one), else two per wavefront
     const bool one = kc <= 4 || (kc > 8 && variant == VAR_FP8_ROW);
     const int64_t rows = (kThreads / kWave) * (one ? 1 : 2);   // rows per workgroup
     const int64_t g = (ntot + rows - 1) / rows;
