@@ -77,6 +77,13 @@ def parse():
                          "projection M=16 N=K=4096 (32 weight copies) and the W8A8 Llama layer set at M=4, 16, "
                          "32 (4 layers each), one qlin_linear call per input, three eager passes each; "
                          "prints no JSON")
+    ap.add_argument("--decode-workload", action="store_true",
+                    help="for kernel traces and counters of the one-token path of every scheme: a 1 GiB "
+                         "copy (counter calibration), then for each of --decode-schemes, 8 layers of the projection set at M=1 (Qwen3-8B shapes for "
+                         "fp8_block), one qlin_linear launch per layer input, three eager passes each; "
+                         "prints no JSON")
+    ap.add_argument("--decode-schemes", default="int8,fp8_row,fp8_block",
+                    help="comma list of int8, fp8_row, fp8_block for --decode-workload")
     ap.add_argument("--smallm-schemes", default="int8",
                     help="comma list of int8, fp8_row, fp8_block for --smallm-workload (int8 also runs the "
                          "16 x 4096 x 4096 projection; fp8_block uses the Qwen3-8B shapes)")
@@ -563,6 +570,20 @@ def main():
                 log(f"prefill workload {variant}{' packed' if run is packed else ''}: M={M}, 4 layers, "
                     f"{len(run.calls)} calls per pass x3, {ops} ops per pass")
                 del keep, fused, packed, packed_sg, packed_all, run
+        return
+    if args.decode_workload:
+        copy_calibration()
+        for sname in args.decode_schemes.split(","):
+            scheme = {"int8": Q.SCHEME_W8A8, "fp8_row": Q.SCHEME_FP8_ROWWISE, "fp8_block": Q.SCHEME_FP8_BLOCK}[sname]
+            shapes = W.QWEN3_8B if sname == "fp8_block" else W.LLAMA_8B
+            Lr, nbytes, ops, keep = layer_set(torch, Q, W, scheme, shapes, 1, 8, dev, 700)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                Lr.run()
+            torch.cuda.synchronize()
+            log(f"decode workload: {sname} M=1, 8 layers, {len(Lr.calls)} launches per pass x3, "
+                f"{nbytes} algorithmic bytes per pass")
+            del Lr, keep
         return
     if args.smallm_workload:
         copy_calibration()
