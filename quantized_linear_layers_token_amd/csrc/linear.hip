@@ -44,6 +44,10 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     __shared__ uint32_t red[kThreads / kWave];
     __shared__ __attribute__((aligned(16))) uint8_t xq[SL * 1024];
     __shared__ float gsc[KC * 8];   // block scheme: one scale per 128-input group
+    // block scheme, rows of an even number of KiB: each wavefront's 2 KiB chunk of
+    // a row, 128-byte groups with their 16-byte pieces rotated by the group index
+    constexpr bool BPAIR = V == VAR_FP8_BLOCK && KC % 2 == 0;
+    __shared__ __attribute__((aligned(16))) uint8_t wst[BPAIR ? kThreads / kWave : 1][BPAIR ? 2048 : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -192,9 +196,14 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
     const float s_tok = gsc[0];
 
     // Block FP8 on the matrix cores needs the four lanes of MFMA row i (lanes
-    // i, i + 16, i + 32, i + 48) to hold one 128-input group: lane l takes the
-    // 16 bytes loaded by lane 4 (l % 16) + l / 16, so row i holds bytes
-    // [64 i, 64 i + 64) of each KiB, half of group i / 2.
+    // i, i + 16, i + 32, i + 48) to hold one 128-input group.  Rows of an even
+    // number of KiB (BPAIR) pass each 2 KiB chunk through the wavefront's LDS
+    // buffer, so row i holds all of group i of the chunk and one MFMA covers
+    // 2 KiB; measured against the per-KiB form below, Qwen3-8B block decode
+    // 1.513-1.521 -> 1.448-1.457 ms per token (alternated on one box).  Rows of
+    // an odd number of KiB: lane l takes (ds_bpermute) the 16 bytes loaded by
+    // lane 4 (l % 16) + l / 16, so row i holds bytes [64 i, 64 i + 64) of each
+    // KiB, half of group i / 2, one MFMA per KiB with half its K slots zero.
     const int paddr = 4 * (4 * (lane & 15) + (lane >> 4));
     auto bperm = [&](const v4u& v) {
         return v4u{(unsigned)__builtin_amdgcn_ds_bpermute(paddr, (int)v.x),
@@ -241,6 +250,37 @@ __global__ __launch_bounds__(kThreads) void linear_decode_kernel(
                     c = mfma_e4m3(wr[r][2 * q], 2 * q + 1 < SL ? wr[r][2 * q + 1] : v4u{0, 0, 0, 0}, tok(2 * q),
                                   2 * q + 1 < SL ? tok(2 * q + 1) : v4u{0, 0, 0, 0}, c);
                 facc[r] = wave_sum_f32(mfma16_diag(c, lane));
+            } else if constexpr (BPAIR) {
+                // one MFMA per 2 KiB: the chunk goes through this wavefront's LDS
+                // buffer so that MFMA row i (lanes i, i + 16, i + 32, i + 48) holds
+                // the whole group i of the chunk (lane i + 16 p its bytes 32 p ..
+                // 32 p + 31); diagonal element i is then group 16 c + i of the row,
+                // scaled by its s_x * s_w (groups past K meet zero activations)
+                float f[NF];
+#pragma unroll
+                for (int h = 0; h < NF; ++h) f[h] = gx[h] * bf16_lo(fw[r][h]);
+                uint8_t* const wb = wst[wave];
+                const int gi = lane & 15, gp = lane >> 4;
+                float a = 0.0f;
+#pragma unroll
+                for (int c = 0; c < SL / 2; ++c) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int g = 8 * h + (lane >> 3);
+                        *reinterpret_cast<v4u*>(wb + 128 * g + 16 * (((lane & 7) + g) & 7)) = wr[r][2 * c + h];
+                    }
+                    const v4u w0 = *reinterpret_cast<const v4u*>(wb + 128 * gi + 16 * ((2 * gp + gi) & 7));
+                    const v4u w1 = *reinterpret_cast<const v4u*>(wb + 128 * gi + 16 * ((2 * gp + 1 + gi) & 7));
+                    const int o = 2048 * c + 128 * gi + 32 * gp;     // byte offset of the lane's 32 bytes in the row
+                    const v4u x0 = (o >> 4) < k16 ? *reinterpret_cast<const v4u*>(xq + o) : v4u{0, 0, 0, 0};
+                    const v4u x1 = (o >> 4) + 1 < k16 ? *reinterpret_cast<const v4u*>(xq + o + 16) : v4u{0, 0, 0, 0};
+                    const v4f pp = mfma_e4m3(w0, w1, x0, x1, v4f{0.f, 0.f, 0.f, 0.f});
+                    const int g = 16 * c + gi;                        // this lane's diagonal group
+                    const float fg = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (g & 63), __float_as_int(f[(16 * c) / 64])));
+                    a = __builtin_fmaf(mfma16_diag(pp, lane), fg, a);
+                    if (c % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+                }
+                facc[r] = wave_sum_f32(a);
             } else {
                 // one MFMA per KiB (half of its K slots zero): diagonal element i
                 // is half of group 8 q + i / 2, scaled by s_x[group] * s_w[row
